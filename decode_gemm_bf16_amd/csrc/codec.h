@@ -1,0 +1,60 @@
+// Host-side encoder of the exponent codec (Unweight page, sections 三, 四, 六).
+//
+// Builds, from a row-major bf16 matrix, the serial sign+mantissa stream, the
+// 4-bit palette form with its raw-group tables, and the 12-bit length-limited
+// canonical Huffman form with its chunk bit offsets and decode table.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace uw {
+
+constexpr int kBrickRows = 16;
+constexpr int kBrickCols = 64;
+constexpr int kBrickWeights = kBrickRows * kBrickCols;  // 1024
+constexpr int kRun = 16;                                // weights of one row per run
+constexpr int kChunk = 256;                             // Huffman symbols per chunk
+constexpr int kLmax = 12;                               // longest code, bits
+constexpr int kLutSize = 1 << kLmax;                    // decode table entries
+constexpr int kStreamPadWords = 4;                      // zero words after the stream
+
+struct HostFormat {
+  int64_t rows = 0, cols = 0;
+  uint32_t formats = 0;
+  uint64_t hist[256] = {};
+  uint32_t distinct = 0;
+  std::vector<uint8_t> sm;  // serial sign+mantissa bytes
+
+  // palette form
+  uint8_t palette[16] = {};
+  std::vector<uint8_t> nib;         // serial 4-bit codes, 8 codes per 4 bytes
+  std::vector<uint32_t> rawmap;     // per brick: bit r = row r's group is raw
+  std::vector<uint32_t> rawbefore;  // per brick: raw groups in earlier bricks
+  std::vector<uint8_t> side;        // 64 original exponents per raw group
+  uint64_t n_raw = 0;
+
+  // Huffman form
+  uint8_t lengths[256] = {};
+  uint32_t codes[256] = {};
+  std::vector<uint32_t> words;      // payload + kStreamPadWords zero words
+  uint64_t stream_bits = 0;
+  std::vector<uint32_t> offsets;    // first bit of each chunk
+  std::vector<uint16_t> lut;        // 4096 entries: symbol | length << 8
+
+  uint64_t n() const { return uint64_t(rows) * uint64_t(cols); }
+  uint64_t bricks() const { return n() / kBrickWeights; }
+  double bpw_palette() const;
+  double bpw_huffman() const;
+};
+
+// Returns an empty string on success, else the reason.  `formats` uses the
+// UW_FMT_* flags of uw.h (palette tables are built for PALETTE or RAWAUX).
+std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t formats,
+                        HostFormat& out);
+
+// Length-limited optimal code lengths over a 256-symbol histogram.
+void limited_code_lengths(const uint64_t hist[256], int lmax, uint8_t lengths[256]);
+
+}  // namespace uw

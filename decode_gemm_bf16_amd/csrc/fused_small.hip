@@ -1,0 +1,165 @@
+// Fused reconstruct-matmul for small batches (1..64 tokens) on gfx950.
+//
+// Unweight page, section 七 (the reconstructing matmul) and section 五 (weights
+// are rebuilt on chip and never written back to HBM).  The pages' Hopper design
+// (TMA producer filling a shared-memory ring, consumers issuing WGMMA) is not
+// used: here every lane streams its own 16 B of sign+mantissa bytes and 8 B of
+// 4-bit codes (or 16 B of exponent bytes) straight from HBM into registers, the
+// bf16 words are rebuilt in registers (recon.h) and fed as the A operand of
+// v_mfma_f32_16x16x32_bf16; activations are the B operand.  With weights as A,
+// a 16-row brick feeds 16 tokens per instruction, so batch 1 and batch 16 cost
+// the same matrix-core time, which is negligible next to the HBM stream.
+//
+// Work split: one workgroup per 16-row brick-row (x `ksplit` slices of K);
+// its waves take every WAVES-th brick along K, so a workgroup sweeps a
+// contiguous stretch of the stream.  Partial sums meet in LDS; with ksplit > 1
+// the slices add into a zeroed Y with float atomics.
+#include "kernels.h"
+#include "recon.h"
+
+namespace uw {
+namespace {
+
+template <int WAVES, int TB, bool EXPM, int UNROLL>
+__global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
+    const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
+    const uint8_t* __restrict__ side, uint32_t lut0, uint32_t lut1, uint32_t lut2, uint32_t lut3,
+    const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols, int ksplit) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;  // row inside the brick (A operand row) / token inside a block (B column)
+  const int q = lane >> 4;  // which 16-column quarter of the brick
+  const int kbn = cols >> 6;
+  const int lo = (int)(((int64_t)blockIdx.y * kbn) / ksplit);
+  const int hi = (int)(((int64_t)(blockIdx.y + 1) * kbn) / ksplit);
+  const size_t brick_row0 = (size_t)blockIdx.x * kbn;
+  const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
+
+  f32x4 acc[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb0 = lo + wave; kb0 < hi; kb0 += WAVES * UNROLL) {
+    u32x4 s[UNROLL];
+    u32x4 e[UNROLL];
+    u32x2 n[UNROLL];
+    uint2 m[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int kb = kb0 + u * WAVES;
+      if (kb < hi) {
+        const size_t b = brick_row0 + kb;
+        s[u] = *(const u32x4*)(sm + b * 1024 + lane * 16);
+        if (EXPM) {
+          e[u] = *(const u32x4*)(codes + b * 1024 + lane * 16);
+        } else {
+          n[u] = *(const u32x2*)(codes + b * 512 + lane * 8);
+          m[u] = meta[b];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int kb = kb0 + u * WAVES;
+      if (kb >= hi) break;
+      uint32_t p[8];
+      if (EXPM) {
+        rebuild_exp(s[u], e[u], p);
+      } else {
+        rebuild_palette(s[u], n[u], lut, p);
+        const uint32_t map = m[u].x;
+        if (map) {                     // some row of this brick is stored raw
+          if ((map >> r) & 1u) {
+            const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
+            const u32x4 ev = *(const u32x4*)(side + ((size_t)m[u].y + rank) * 64 + q * 16);
+            rebuild_exp(s[u], ev, p);
+          }
+        }
+      }
+      const bf16x8 a0 = as_bf16x8(p[0], p[1], p[2], p[3]);
+      const bf16x8 a1 = as_bf16x8(p[4], p[5], p[6], p[7]);
+      const int kx = kb * 64 + q * 16;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const int tok = t * 16 + r;
+        u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+        if (tok < tokens) {
+          const uint16_t* xp = x + (size_t)tok * cols + kx;
+          x0 = *(const u32x4*)xp;
+          x1 = *(const u32x4*)(xp + 8);
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x0), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x1), acc[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // D layout of the 16x16 result: lane l holds rows 4*(l/16)+0..3, column l%16.
+  __shared__ f32x4 red[WAVES][TB][64];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  for (int i = threadIdx.x; i < TB * 64; i += WAVES * 64) {
+    const int t = i >> 6, l = i & 63;
+    f32x4 sum = red[0][t][l];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) sum += red[w][t][l];
+    const int tok = t * 16 + (l & 15);
+    if (tok >= tokens) continue;
+    float* yp = y + (size_t)tok * rows + (size_t)blockIdx.x * 16 + 4 * (l >> 4);
+    if (ksplit == 1) {
+      *(f32x4*)yp = sum;
+    } else {
+      atomicAdd(yp + 0, sum.x);
+      atomicAdd(yp + 1, sum.y);
+      atomicAdd(yp + 2, sum.z);
+      atomicAdd(yp + 3, sum.w);
+    }
+  }
+}
+
+template <int WAVES, int TB, bool EXPM, int UNROLL>
+hipError_t launch_one(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
+  dim3 grid((unsigned)(w.rows / 16), (unsigned)ksplit);
+  hipLaunchKernelGGL((fused_small_kernel<WAVES, TB, EXPM, UNROLL>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
+                     w.meta, w.side, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens, (int)w.rows,
+                     (int)w.cols, ksplit);
+  return hipGetLastError();
+}
+
+template <int WAVES, int TB, int UNROLL>
+hipError_t launch_mode(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
+  return w.exp_mode ? launch_one<WAVES, TB, true, UNROLL>(w, x, y, tokens, ksplit, s)
+                    : launch_one<WAVES, TB, false, UNROLL>(w, x, y, tokens, ksplit, s);
+}
+
+template <int WAVES, int UNROLL>
+hipError_t launch_tb(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
+  switch ((tokens + 15) / 16) {
+    case 1: return launch_mode<WAVES, 1, UNROLL>(w, x, y, tokens, ksplit, s);
+    case 2: return launch_mode<WAVES, 2, UNROLL>(w, x, y, tokens, ksplit, s);
+    case 3: return launch_mode<WAVES, 3, UNROLL>(w, x, y, tokens, ksplit, s);
+    default: return launch_mode<WAVES, 4, UNROLL>(w, x, y, tokens, ksplit, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fused_small(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                              hipStream_t s) {
+  if (tokens < 1 || tokens > 64) return hipErrorInvalidValue;
+  const int ks = v.ksplit < 1 ? 1 : v.ksplit;
+  if (ks > 1) {
+    hipError_t e = launch_zero(y, tokens * w.rows, s);
+    if (e != hipSuccess) return e;
+  }
+#define UW_CASE(W, U) \
+  if (v.waves == W && v.unroll == U) return launch_tb<W, U>(w, x, y, tokens, ks, s);
+  UW_CASE(4, 1) UW_CASE(4, 2) UW_CASE(4, 4)
+  UW_CASE(8, 1) UW_CASE(8, 2) UW_CASE(8, 4)
+  UW_CASE(16, 1) UW_CASE(16, 2)
+#undef UW_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace uw

@@ -1,0 +1,61 @@
+// Launchers of the gfx950 kernels (definitions in *.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace uw {
+
+// What a fused kernel reads for W (all per-weight streams in serial brick order).
+struct FusedW {
+  const uint8_t* sm;       // sign+mantissa bytes, 1 per weight
+  const uint8_t* codes;    // palette mode: 4-bit codes (0.5 B/weight); exponent mode: exponent bytes
+  const uint2* meta;       // palette mode: per brick {raw map, raw groups before}
+  const uint8_t* side;     // palette mode: raw groups' exponent bytes
+  uint32_t lut[4];         // palette mode: entry i = rotr8(palette[i], 1) at byte i%4 of lut[i/4]
+  int64_t rows, cols;
+  bool exp_mode;           // codes are exponent bytes (pipeline 2)
+};
+
+// Fused-kernel variants.  Small-batch kernels (tokens <= 64): one workgroup per
+// 16 rows, `waves` waves splitting the K loop, optional split of K across
+// `ksplit` workgroups (atomic accumulation into a zeroed Y).  Large-batch
+// kernels (tokens > 64): see fused_large.hip.
+struct Variant {
+  int kind;    // 0 = small batch, 1 = large batch
+  int waves;   // small: waves per workgroup
+  int ksplit;  // small: workgroups along K
+  int unroll;  // small: bricks in flight per wave
+  int tile;    // large: tile shape id
+};
+int variant_count(int64_t tokens);
+bool variant_get(int64_t tokens, int id, Variant* v);  // id 0 = default for (tokens, shape)
+Variant variant_default(int64_t tokens, int64_t rows, int64_t cols);
+const char* variant_name(int64_t tokens, int id);
+
+hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                        hipStream_t s);
+
+// Huffman decode of every chunk (one lane per 256-symbol chunk).
+enum DecodeEmit { EMIT_BF16 = 0, EMIT_EXP = 1, EMIT_NIBBLE = 2 };
+struct HuffDev {
+  const uint32_t* words;
+  const uint32_t* offsets;
+  const uint16_t* lut;      // 4096 entries: symbol | length << 8
+  const uint8_t* sm;        // EMIT_BF16
+  const uint2* meta;        // EMIT_NIBBLE: per-brick raw map
+  const uint8_t* code_of;   // EMIT_NIBBLE: 256 entries, code of each palette exponent
+  int64_t rows, cols;
+};
+hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipStream_t s);
+
+// Palette form -> bf16 W row-major (decode without a Huffman stream).
+hipError_t launch_palette_decode(const FusedW& w, uint16_t* out, hipStream_t s);
+
+hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+}  // namespace uw

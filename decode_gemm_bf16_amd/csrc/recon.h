@@ -1,0 +1,86 @@
+// Device helpers: rebuild packed bf16 pairs from the stored bytes.
+//
+// A BF16 word (Unweight page, section 三) is sign<<15 | exponent<<7 | mantissa.
+// Its low byte is (exponent & 1)<<7 | mantissa and its high byte is
+// sign<<7 | exponent>>1.  With V = the exponent rotated right by one bit
+// (bit 7 = exponent & 1, bits 6..0 = exponent >> 1) and S = the stored
+// sign+mantissa byte (bit 7 = sign, bits 6..0 = mantissa):
+//     low  byte = (S & 0x7F) | (V & 0x80)
+//     high byte = (S & 0x80) | (V & 0x7F)
+// so four weights take two bit-selects on whole dwords and two byte permutes
+// to become two dwords of bf16 pairs -- no per-weight shifts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace uw {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  // byte i of the result = byte sel.byte[i] of the 8-byte value hi:lo
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// S: 4 sign+mantissa bytes, V: the 4 matching rotated exponents.
+// Returns the bf16 pairs (w0,w1) and (w2,w3).
+__device__ __forceinline__ void assemble_v(uint32_t S, uint32_t V, uint32_t& p01, uint32_t& p23) {
+  const uint32_t L = (S & 0x7F7F7F7Fu) | (V & 0x80808080u);
+  const uint32_t H = (S & 0x80808080u) | (V & 0x7F7F7F7Fu);
+  p01 = perm(H, L, 0x05010400u);
+  p23 = perm(H, L, 0x07030602u);
+}
+
+// Same, from 4 plain exponent bytes E.
+__device__ __forceinline__ void assemble_e(uint32_t S, uint32_t E, uint32_t& p01, uint32_t& p23) {
+  const uint32_t L = (S & 0x7F7F7F7Fu) | ((E << 7) & 0x80808080u);
+  const uint32_t H = (S & 0x80808080u) | ((E >> 1) & 0x7F7F7F7Fu);
+  p01 = perm(H, L, 0x05010400u);
+  p23 = perm(H, L, 0x07030602u);
+}
+
+// 16-entry palette lookup of 8 codes packed in N (byte b: code b low nibble,
+// code b+4 high nibble).  lut[q] holds entries 4q..4q+3.  Low three code bits
+// index two 8-entry halves with one byte permute each; the fourth bit then
+// picks, per byte, the half through a third permute.
+__device__ __forceinline__ void palette_lookup(uint32_t N, const uint32_t lut[4], uint32_t& Va, uint32_t& Vb) {
+  const uint32_t ia = N & 0x07070707u;
+  const uint32_t ib = (N >> 4) & 0x07070707u;
+  const uint32_t sa = ((N >> 1) & 0x04040404u) | 0x03020100u;
+  const uint32_t sb = ((N >> 5) & 0x04040404u) | 0x03020100u;
+  Va = perm(perm(lut[3], lut[2], ia), perm(lut[1], lut[0], ia), sa);
+  Vb = perm(perm(lut[3], lut[2], ib), perm(lut[1], lut[0], ib), sb);
+}
+
+// One lane's 16 weights of a brick -> 8 dwords of bf16 pairs, weights in order.
+__device__ __forceinline__ void rebuild_palette(const u32x4& s, const u32x2& n, const uint32_t lut[4],
+                                                uint32_t p[8]) {
+  uint32_t v0, v1, v2, v3;
+  palette_lookup(n.x, lut, v0, v1);
+  palette_lookup(n.y, lut, v2, v3);
+  assemble_v(s.x, v0, p[0], p[1]);
+  assemble_v(s.y, v1, p[2], p[3]);
+  assemble_v(s.z, v2, p[4], p[5]);
+  assemble_v(s.w, v3, p[6], p[7]);
+}
+
+__device__ __forceinline__ void rebuild_exp(const u32x4& s, const u32x4& e, uint32_t p[8]) {
+  assemble_e(s.x, e.x, p[0], p[1]);
+  assemble_e(s.y, e.y, p[2], p[3]);
+  assemble_e(s.z, e.z, p[4], p[5]);
+  assemble_e(s.w, e.w, p[6], p[7]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+}  // namespace uw

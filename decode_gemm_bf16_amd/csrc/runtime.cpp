@@ -1,0 +1,816 @@
+// C ABI (include/uw.h): handles, device upload, the four pipelines (Unweight
+// page, section 六), side-stream preprocessing (section 八), plans from the
+// autotuner (section 九), the SwiGLU layer and layer-stack runners, and the
+// hipBLASLt call used by pipeline 1 and by the uncompressed baseline.
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <hipblaslt/hipblaslt.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/uw.h"
+#include "codec.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+uw_status fail(uw_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define UW_HIP(call)                                                                  \
+  do {                                                                                \
+    hipError_t e_ = (call);                                                           \
+    if (e_ != hipSuccess) return fail(UW_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Last-consumer event of each scratch buffer: a preprocessing step on a side
+// stream must not overwrite scratch that the main stream still reads.
+std::mutex g_scratch_mu;
+std::map<void*, hipEvent_t> g_scratch_consumed;
+
+hipEvent_t scratch_event(void* p) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_consumed.find(p);
+  if (it != g_scratch_consumed.end()) return it->second;
+  hipEvent_t ev = nullptr;
+  if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return nullptr;
+  g_scratch_consumed[p] = ev;
+  return ev;
+}
+
+void scratch_forget(void* p) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_consumed.find(p);
+  if (it != g_scratch_consumed.end()) {
+    (void)hipEventDestroy(it->second);
+    g_scratch_consumed.erase(it);
+  }
+}
+
+// ---- hipBLASLt (pipeline 1's library GEMM and the uncompressed baseline) ----
+struct GemmPlan {
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+  hipblasLtMatmulAlgo_t algo;
+};
+std::mutex g_blas_mu;
+hipblasLtHandle_t g_blas = nullptr;
+void* g_blas_ws = nullptr;
+constexpr size_t kBlasWs = size_t(64) << 20;
+std::map<std::tuple<int64_t, int64_t, int64_t>, GemmPlan> g_plans;
+
+uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, int64_t n, int64_t k,
+                    hipStream_t s) {
+  std::lock_guard<std::mutex> lk(g_blas_mu);
+  if (!g_blas) {
+    if (hipblasLtCreate(&g_blas) != HIPBLAS_STATUS_SUCCESS) return fail(UW_ERR_HIP, "hipblasLtCreate failed");
+    if (hipMalloc(&g_blas_ws, kBlasWs) != hipSuccess) return fail(UW_ERR_OOM, "hipBLASLt workspace");
+  }
+  auto key = std::make_tuple(m, n, k);
+  auto it = g_plans.find(key);
+  if (it == g_plans.end()) {
+    // Column-major view: Y^T[n, m] = W[n, k] * X^T[k, m]; W row-major [n, k] is
+    // a column-major k x n matrix used transposed, X row-major is k x m.
+    GemmPlan p;
+    hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+    bool ok = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb) ==
+                  HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.a, HIP_R_16BF, k, n, k) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.b, HIP_R_16BF, k, m, k) == HIPBLAS_STATUS_SUCCESS &&
+              hipblasLtMatrixLayoutCreate(&p.c, HIP_R_32F, n, m, n) == HIPBLAS_STATUS_SUCCESS;
+    if (!ok) return fail(UW_ERR_HIP, "hipBLASLt descriptor setup failed");
+    hipblasLtMatmulPreference_t pref = nullptr;
+    uint64_t ws = kBlasWs;
+    hipblasLtMatmulPreferenceCreate(&pref);
+    hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof ws);
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int got = 0;
+    hipblasStatus_t hs =
+        hipblasLtMatmulAlgoGetHeuristic(g_blas, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &got);
+    hipblasLtMatmulPreferenceDestroy(pref);
+    if (hs != HIPBLAS_STATUS_SUCCESS || got < 1)
+      return fail(UW_ERR_HIP, "hipBLASLt has no bf16->f32 algorithm for m=%lld n=%lld k=%lld", (long long)m,
+                  (long long)n, (long long)k);
+    p.algo = res[0].algo;
+    it = g_plans.emplace(key, p).first;
+  }
+  const float alpha = 1.f, beta = 0.f;
+  GemmPlan& p = it->second;
+  hipblasStatus_t hs = hipblasLtMatmul(g_blas, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.c, y, p.c, &p.algo,
+                                       g_blas_ws, kBlasWs, s);
+  if (hs != HIPBLAS_STATUS_SUCCESS) return fail(UW_ERR_HIP, "hipblasLtMatmul failed (%d)", (int)hs);
+  return UW_OK;
+}
+
+}  // namespace
+
+struct uw_matrix {
+  uw::HostFormat hf;
+  bool host_only = false;
+  int64_t rows = 0, cols = 0;
+  uint32_t formats = 0;
+  // one device allocation holding every resident stream
+  void* dmem = nullptr;
+  size_t dmem_bytes = 0;
+  uint8_t* d_sm = nullptr;
+  uint8_t* d_nib = nullptr;
+  uint2* d_meta = nullptr;
+  uint8_t* d_side = nullptr;
+  uint8_t* d_code_of = nullptr;
+  uint32_t* d_words = nullptr;
+  uint32_t* d_offsets = nullptr;
+  uint16_t* d_lut = nullptr;
+  uint32_t lut_v[4] = {};
+  uint64_t words_total = 0;  // payload + padding words on the device
+  hipStream_t main = nullptr, side = nullptr;
+  void* scratch = nullptr;
+  size_t scratch_cap = 0;
+  bool own_scratch = false;
+  hipEvent_t prep_done = nullptr;
+  int prep_pipeline = 0;  // pipeline whose preprocessed scratch is pending
+  int plan_n = 0;
+  int32_t plan_tok[16] = {}, plan_pipe[16] = {}, plan_var[16] = {};
+  int variant = 0;
+
+  bool has(uint32_t f) const { return (formats & f) != 0; }
+  bool has_pal_tables() const { return has(UW_FMT_PALETTE) || has(UW_FMT_RAWAUX); }
+  size_t scratch_need(int p) const {
+    const size_t n = size_t(rows) * size_t(cols);
+    switch (p) {
+      case 1: return align256(2 * n);
+      case 2: return align256(n);
+      case 3: return align256(n / 2);
+      default: return 0;
+    }
+  }
+};
+
+namespace {
+
+uw::FusedW fused_view(const uw_matrix* h, bool exp_mode, const uint8_t* codes) {
+  uw::FusedW f;
+  f.sm = h->d_sm;
+  f.codes = codes;
+  f.meta = h->d_meta;
+  f.side = h->d_side;
+  for (int i = 0; i < 4; ++i) f.lut[i] = h->lut_v[i];
+  f.rows = h->rows;
+  f.cols = h->cols;
+  f.exp_mode = exp_mode;
+  return f;
+}
+
+uw::HuffDev huff_view(const uw_matrix* h) {
+  uw::HuffDev d;
+  d.words = h->d_words;
+  d.offsets = h->d_offsets;
+  d.lut = h->d_lut;
+  d.sm = h->d_sm;
+  d.meta = h->d_meta;
+  d.code_of = h->d_code_of;
+  d.rows = h->rows;
+  d.cols = h->cols;
+  return d;
+}
+
+uw_status check_pipeline(const uw_matrix* h, int p) {
+  switch (p) {
+    case 1:
+    case 2:
+      if (!h->has(UW_FMT_HUFFMAN)) return fail(UW_ERR_UNSUPPORTED, "pipeline %d needs the Huffman format", p);
+      return UW_OK;
+    case 3:
+      if (!h->has(UW_FMT_HUFFMAN) || !h->has_pal_tables())
+        return fail(UW_ERR_UNSUPPORTED, "pipeline 3 needs the Huffman format and the palette tables");
+      return UW_OK;
+    case 4:
+      if (!h->has(UW_FMT_PALETTE)) return fail(UW_ERR_UNSUPPORTED, "pipeline 4 needs the palette format");
+      return UW_OK;
+    default:
+      return fail(UW_ERR_INVALID_ARG, "unknown pipeline %d", p);
+  }
+}
+
+int resolve_pipeline(const uw_matrix* h, int64_t tokens, int pipeline, int* variant) {
+  *variant = h->variant;
+  if (pipeline != UW_P_AUTO) return pipeline;
+  for (int i = 0; i < h->plan_n; ++i)
+    if (tokens <= h->plan_tok[i]) {
+      *variant = h->plan_var[i];
+      return h->plan_pipe[i];
+    }
+  *variant = 0;
+  if (h->has(UW_FMT_PALETTE)) return 4;
+  if (h->has(UW_FMT_HUFFMAN) && h->has_pal_tables()) return 3;
+  return 1;
+}
+
+uw_status ensure_scratch(uw_matrix* h, int p) {
+  const size_t need = h->scratch_need(p);
+  if (h->scratch && h->scratch_cap >= need) return UW_OK;
+  if (h->scratch && !h->own_scratch)
+    return fail(UW_ERR_INVALID_ARG, "bound scratch holds %zu bytes, pipeline %d needs %zu", h->scratch_cap, p, need);
+  if (h->scratch) {
+    UW_HIP(hipStreamSynchronize(h->main));
+    if (h->side != h->main) UW_HIP(hipStreamSynchronize(h->side));
+    scratch_forget(h->scratch);
+    (void)hipFree(h->scratch);
+    h->scratch = nullptr;
+  }
+  if (hipMalloc(&h->scratch, need) != hipSuccess) {
+    h->scratch = nullptr;
+    return fail(UW_ERR_OOM, "scratch allocation of %zu bytes failed", need);
+  }
+  h->scratch_cap = need;
+  h->own_scratch = true;
+  return UW_OK;
+}
+
+uw_status launch_preprocess(uw_matrix* h, int p, hipStream_t s) {
+  const uw::HuffDev d = huff_view(h);
+  const uw::DecodeEmit emit = p == 1 ? uw::EMIT_BF16 : p == 2 ? uw::EMIT_EXP : uw::EMIT_NIBBLE;
+  UW_HIP(uw::launch_huff_decode(d, emit, h->scratch, s));
+  return UW_OK;
+}
+
+// Make the main stream's copy of the preprocessed scratch ready.
+uw_status prepare(uw_matrix* h, int p) {
+  uw_status st = ensure_scratch(h, p);
+  if (st != UW_OK) return st;
+  if (h->prep_pipeline == p) {
+    UW_HIP(hipStreamWaitEvent(h->main, h->prep_done, 0));
+    h->prep_pipeline = 0;
+    return UW_OK;
+  }
+  h->prep_pipeline = 0;
+  return launch_preprocess(h, p, h->main);
+}
+
+uw_status mark_consumed(uw_matrix* h) {
+  hipEvent_t ev = scratch_event(h->scratch);
+  if (!ev) return fail(UW_ERR_HIP, "event creation failed");
+  UW_HIP(hipEventRecord(ev, h->main));
+  return UW_OK;
+}
+
+uw_status matmul_impl(uw_matrix* h, const uint16_t* x, float* y, int64_t tokens, int pipeline) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
+  if (!x || !y) return fail(UW_ERR_INVALID_ARG, "null activation or output pointer");
+  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
+  if (tokens > (int64_t(1) << 24)) return fail(UW_ERR_INVALID_ARG, "tokens too large");
+  int var = 0;
+  const int p = resolve_pipeline(h, tokens, pipeline, &var);
+  uw_status st = check_pipeline(h, p);
+  if (st != UW_OK) return st;
+  uw::Variant v = uw::variant_default(tokens, h->rows, h->cols);
+  if (var != 0 && !uw::variant_get(tokens, var, &v))
+    return fail(UW_ERR_INVALID_ARG, "variant %d does not exist for %lld tokens", var, (long long)tokens);
+  switch (p) {
+    case 4:
+      UW_HIP(uw::launch_fused(fused_view(h, false, h->d_nib), x, y, tokens, v, h->main));
+      return UW_OK;
+    case 3:
+    case 2: {
+      if ((st = prepare(h, p)) != UW_OK) return st;
+      UW_HIP(uw::launch_fused(fused_view(h, p == 2, (const uint8_t*)h->scratch), x, y, tokens, v, h->main));
+      return mark_consumed(h);
+    }
+    case 1: {
+      if ((st = prepare(h, 1)) != UW_OK) return st;
+      if ((st = gemm_bf16(x, (const uint16_t*)h->scratch, y, tokens, h->rows, h->cols, h->main)) != UW_OK) return st;
+      return mark_consumed(h);
+    }
+  }
+  return fail(UW_ERR_INVALID_ARG, "unknown pipeline %d", p);
+}
+
+template <class T>
+T* carve(uint8_t*& cur, size_t bytes) {
+  T* p = reinterpret_cast<T*>(cur);
+  cur += align256(bytes);
+  return p;
+}
+
+uw_status upload(uw_matrix* h) {
+  const uw::HostFormat& f = h->hf;
+  const uint64_t n = f.n();
+  const uint64_t nb = f.bricks();
+  size_t total = align256(n);  // sm
+  const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
+  if (pal) total += align256(n / 2);
+  if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64)) + align256(256);
+  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + align256(uw::kLutSize * 2);
+  if (hipMalloc(&h->dmem, total) != hipSuccess) {
+    h->dmem = nullptr;
+    return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", total);
+  }
+  h->dmem_bytes = total;
+  uint8_t* cur = static_cast<uint8_t*>(h->dmem);
+  h->d_sm = carve<uint8_t>(cur, n);
+  UW_HIP(hipMemcpy(h->d_sm, f.sm.data(), n, hipMemcpyHostToDevice));
+  if (pal) {
+    h->d_nib = carve<uint8_t>(cur, n / 2);
+    UW_HIP(hipMemcpy(h->d_nib, f.nib.data(), n / 2, hipMemcpyHostToDevice));
+  }
+  if (tabs || huf) {
+    // per-brick {raw map, raw groups before}; all zero for a Huffman-only matrix
+    std::vector<uint2> meta(nb, uint2{0, 0});
+    if (tabs)
+      for (uint64_t b = 0; b < nb; ++b) meta[b] = uint2{f.rawmap[b], f.rawbefore[b]};
+    h->d_meta = carve<uint2>(cur, nb * 8);
+    UW_HIP(hipMemcpy(h->d_meta, meta.data(), nb * 8, hipMemcpyHostToDevice));
+    h->d_side = carve<uint8_t>(cur, std::max<size_t>(f.side.size(), 64));
+    if (!f.side.empty()) UW_HIP(hipMemcpy(h->d_side, f.side.data(), f.side.size(), hipMemcpyHostToDevice));
+    uint8_t code_of[256];
+    std::memset(code_of, 0, sizeof code_of);
+    if (tabs) {
+      const int used = std::min<int>(16, int(f.distinct));
+      for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
+    }
+    h->d_code_of = carve<uint8_t>(cur, 256);
+    UW_HIP(hipMemcpy(h->d_code_of, code_of, 256, hipMemcpyHostToDevice));
+  }
+  if (huf) {
+    h->d_words = carve<uint32_t>(cur, f.words.size() * 4);
+    UW_HIP(hipMemcpy(h->d_words, f.words.data(), f.words.size() * 4, hipMemcpyHostToDevice));
+    h->d_offsets = carve<uint32_t>(cur, f.offsets.size() * 4);
+    UW_HIP(hipMemcpy(h->d_offsets, f.offsets.data(), f.offsets.size() * 4, hipMemcpyHostToDevice));
+    h->d_lut = carve<uint16_t>(cur, uw::kLutSize * 2);
+    UW_HIP(hipMemcpy(h->d_lut, f.lut.data(), uw::kLutSize * 2, hipMemcpyHostToDevice));
+    h->words_total = f.words.size();
+  }
+  if (tabs) {
+    // palette entry i, exponent rotated right by one bit, at byte i%4 of lut_v[i/4]
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t e = f.palette[i];
+      const uint32_t v = ((e >> 1) | (e << 7)) & 0xFFu;
+      h->lut_v[i / 4] |= v << (8 * (i % 4));
+    }
+  }
+  UW_HIP(hipEventCreateWithFlags(&h->prep_done, hipEventDisableTiming));
+  return UW_OK;
+}
+
+void release_host_streams(uw::HostFormat& f) {
+  std::vector<uint8_t>().swap(f.sm);
+  std::vector<uint8_t>().swap(f.nib);
+  std::vector<uint8_t>().swap(f.side);
+  std::vector<uint32_t>().swap(f.words);
+  // offsets, rawmap/rawbefore and lut are kept small enough? they are dropped too
+  std::vector<uint32_t>().swap(f.offsets);
+  std::vector<uint32_t>().swap(f.rawmap);
+  std::vector<uint32_t>().swap(f.rawbefore);
+  std::vector<uint16_t>().swap(f.lut);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* uw_last_error(void) { return g_err.c_str(); }
+
+uw_status uw_encode(const uint16_t* w_host, int64_t rows, int64_t cols, uint32_t formats, uw_handle* out) {
+  if (!out) return fail(UW_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  if (!w_host) return fail(UW_ERR_INVALID_ARG, "null weight pointer");
+  const uint32_t fmt = formats & 0x7u;
+  if (!fmt) return fail(UW_ERR_INVALID_ARG, "no format requested");
+  if (formats & ~(0x7u | UW_ENC_HOST_ONLY)) return fail(UW_ERR_INVALID_ARG, "unknown format flags 0x%x", formats);
+  if (rows <= 0 || cols <= 0 || rows % 16 || cols % 64)
+    return fail(UW_ERR_SHAPE, "shape %lldx%lld: rows must be a multiple of 16 and cols of 64", (long long)rows,
+                (long long)cols);
+  uw_matrix* h = new (std::nothrow) uw_matrix;
+  if (!h) return fail(UW_ERR_OOM, "host allocation failed");
+  h->rows = rows;
+  h->cols = cols;
+  h->formats = fmt;
+  h->host_only = (formats & UW_ENC_HOST_ONLY) != 0;
+  std::string err;
+  try {
+    err = uw::encode_host(w_host, rows, cols, fmt, h->hf);
+  } catch (const std::bad_alloc&) {
+    delete h;
+    return fail(UW_ERR_OOM, "host allocation failed during encode");
+  }
+  if (!err.empty()) {
+    delete h;
+    return fail(err.find("2^32") != std::string::npos ? UW_ERR_FORMAT : UW_ERR_SHAPE, "%s", err.c_str());
+  }
+  if (!h->host_only) {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+      delete h;
+      return fail(UW_ERR_NO_DEVICE, "no HIP device");
+    }
+    uw_status st = upload(h);
+    if (st != UW_OK) {
+      if (h->dmem) (void)hipFree(h->dmem);
+      if (h->prep_done) (void)hipEventDestroy(h->prep_done);
+      delete h;
+      return st;
+    }
+    release_host_streams(h->hf);
+  }
+  *out = h;
+  return UW_OK;
+}
+
+uw_status uw_decode(uw_handle h, uint16_t* w_dev_out) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
+  if (!w_dev_out) return fail(UW_ERR_INVALID_ARG, "null output pointer");
+  if (h->has(UW_FMT_HUFFMAN)) {
+    UW_HIP(uw::launch_huff_decode(huff_view(h), uw::EMIT_BF16, w_dev_out, h->main));
+  } else {
+    UW_HIP(uw::launch_palette_decode(fused_view(h, false, h->d_nib), w_dev_out, h->main));
+  }
+  return UW_OK;
+}
+
+uw_status uw_matmul(uw_handle h, const uint16_t* x_dev, float* y_dev, int64_t tokens, int pipeline) {
+  return matmul_impl(h, x_dev, y_dev, tokens, pipeline);
+}
+
+uw_status uw_preprocess(uw_handle h, int pipeline) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
+  if (pipeline < 1 || pipeline > 3) return fail(UW_ERR_UNSUPPORTED, "pipeline %d has no preprocessing", pipeline);
+  uw_status st = check_pipeline(h, pipeline);
+  if (st != UW_OK) return st;
+  if ((st = ensure_scratch(h, pipeline)) != UW_OK) return st;
+  hipEvent_t consumed = scratch_event(h->scratch);
+  if (!consumed) return fail(UW_ERR_HIP, "event creation failed");
+  UW_HIP(hipStreamWaitEvent(h->side, consumed, 0));
+  if ((st = launch_preprocess(h, pipeline, h->side)) != UW_OK) return st;
+  UW_HIP(hipEventRecord(h->prep_done, h->side));
+  h->prep_pipeline = pipeline;
+  return UW_OK;
+}
+
+uw_status uw_set_streams(uw_handle h, void* main_stream, void* side_stream) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  h->main = static_cast<hipStream_t>(main_stream);
+  h->side = side_stream ? static_cast<hipStream_t>(side_stream) : h->main;
+  return UW_OK;
+}
+
+uw_status uw_set_scratch(uw_handle h, void* scratch_dev, size_t bytes) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (!scratch_dev || (reinterpret_cast<uintptr_t>(scratch_dev) & 255))
+    return fail(UW_ERR_INVALID_ARG, "scratch must be a non-null 256-byte aligned device pointer");
+  if (h->scratch && h->own_scratch) {
+    if (hipDeviceSynchronize() != hipSuccess) return fail(UW_ERR_HIP, "synchronize failed");
+    scratch_forget(h->scratch);
+    (void)hipFree(h->scratch);
+  }
+  h->scratch = scratch_dev;
+  h->scratch_cap = bytes;
+  h->own_scratch = false;
+  h->prep_pipeline = 0;
+  return UW_OK;
+}
+
+uw_status uw_set_plan(uw_handle h, const int32_t* max_tokens, const int32_t* pipeline, const int32_t* variant,
+                      int32_t n) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (n < 0 || n > 16) return fail(UW_ERR_INVALID_ARG, "plan size %d out of range", n);
+  if (n && (!max_tokens || !pipeline || !variant)) return fail(UW_ERR_INVALID_ARG, "null plan arrays");
+  for (int i = 0; i < n; ++i) {
+    if (pipeline[i] < 1 || pipeline[i] > 4) return fail(UW_ERR_INVALID_ARG, "plan pipeline %d", pipeline[i]);
+    uw_status st = check_pipeline(h, pipeline[i]);
+    if (st != UW_OK) return st;
+    if (variant[i] < 0 || variant[i] >= uw::variant_count(max_tokens[i]))
+      return fail(UW_ERR_INVALID_ARG, "plan variant %d", variant[i]);
+  }
+  for (int i = 0; i < n; ++i) {
+    h->plan_tok[i] = max_tokens[i];
+    h->plan_pipe[i] = pipeline[i];
+    h->plan_var[i] = variant[i];
+  }
+  h->plan_n = n;
+  return UW_OK;
+}
+
+uw_status uw_set_variant(uw_handle h, int32_t variant) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (variant < 0) return fail(UW_ERR_INVALID_ARG, "variant %d", variant);
+  h->variant = variant;
+  return UW_OK;
+}
+
+const char* uw_variant_name(int64_t tokens, int32_t variant) { return uw::variant_name(tokens, variant); }
+
+uw_status uw_query(uw_handle h, uw_info* o) {
+  if (!h || !o) return fail(UW_ERR_INVALID_ARG, "null argument");
+  std::memset(o, 0, sizeof *o);
+  const uw::HostFormat& f = h->hf;
+  o->rows = h->rows;
+  o->cols = h->cols;
+  o->formats = h->formats;
+  o->chunk = uw::kChunk;
+  o->lmax = uw::kLmax;
+  o->distinct_exponents = f.distinct;
+  std::memcpy(o->palette, f.palette, 16);
+  std::memcpy(o->code_lengths, f.lengths, 256);
+  o->raw_groups = f.n_raw;
+  o->groups = f.n() / 64;
+  o->stream_bits = f.stream_bits;
+  o->stream_words = (f.stream_bits + 31) / 32;
+  o->bpw_palette = h->has_pal_tables() ? f.bpw_palette() : 0.0;
+  o->bpw_huffman = h->has(UW_FMT_HUFFMAN) ? f.bpw_huffman() : 0.0;
+  // what this handle stores
+  const double n = double(f.n());
+  double bits = 8.0 * n;
+  if (h->has(UW_FMT_PALETTE)) bits += 4.0 * n + 128.0;
+  if (h->has_pal_tables()) bits += 512.0 * double(f.n_raw) + 64.0 * double(f.bricks());
+  if (h->has(UW_FMT_HUFFMAN))
+    bits += 32.0 * double(o->stream_words) + 32.0 * double((f.n() + uw::kChunk - 1) / uw::kChunk) + 2048.0;
+  o->bpw_resident = bits / n;
+  o->resident_bytes = h->dmem_bytes;
+  for (int p = 1; p <= 4; ++p) o->scratch_bytes[p] = h->scratch_need(p);
+  return UW_OK;
+}
+
+uw_status uw_export(uw_handle h, int which, void* dst, size_t cap, size_t* len) {
+  if (!h || !len) return fail(UW_ERR_INVALID_ARG, "null argument");
+  const uw::HostFormat& f = h->hf;
+  const uint64_t n = f.n(), nb = f.bricks();
+  const void* host = nullptr;
+  const void* dev = nullptr;
+  size_t bytes = 0;
+  std::vector<uint32_t> tmp;
+  switch (which) {
+    case UW_STREAM_SM: bytes = n; host = f.sm.data(); dev = h->d_sm; break;
+    case UW_STREAM_NIBBLES:
+      if (!h->has(UW_FMT_PALETTE)) return fail(UW_ERR_UNSUPPORTED, "no palette codes");
+      bytes = n / 2; host = f.nib.data(); dev = h->d_nib; break;
+    case UW_STREAM_RAWMAP:
+    case UW_STREAM_RAWBEFORE:
+      if (!h->has_pal_tables()) return fail(UW_ERR_UNSUPPORTED, "no palette tables");
+      bytes = nb * 4;
+      if (h->host_only) {
+        host = which == UW_STREAM_RAWMAP ? f.rawmap.data() : f.rawbefore.data();
+      } else {
+        std::vector<uint2> meta(nb);
+        UW_HIP(hipMemcpy(meta.data(), h->d_meta, nb * 8, hipMemcpyDeviceToHost));
+        tmp.resize(nb);
+        for (uint64_t b = 0; b < nb; ++b) tmp[b] = which == UW_STREAM_RAWMAP ? meta[b].x : meta[b].y;
+        host = tmp.data();
+      }
+      break;
+    case UW_STREAM_SIDE:
+      if (!h->has_pal_tables()) return fail(UW_ERR_UNSUPPORTED, "no palette tables");
+      bytes = f.n_raw * 64; host = f.side.data(); dev = h->d_side; break;
+    case UW_STREAM_WORDS:
+      if (!h->has(UW_FMT_HUFFMAN)) return fail(UW_ERR_UNSUPPORTED, "no Huffman stream");
+      bytes = ((f.stream_bits + 31) / 32) * 4; host = f.words.data(); dev = h->d_words; break;
+    case UW_STREAM_OFFSETS:
+      if (!h->has(UW_FMT_HUFFMAN)) return fail(UW_ERR_UNSUPPORTED, "no Huffman stream");
+      bytes = ((n + uw::kChunk - 1) / uw::kChunk) * 4; host = f.offsets.data(); dev = h->d_offsets; break;
+    case UW_STREAM_PALETTE:
+      if (!h->has_pal_tables()) return fail(UW_ERR_UNSUPPORTED, "no palette");
+      bytes = 16; host = f.palette; break;
+    case UW_STREAM_LENGTHS:
+      if (!h->has(UW_FMT_HUFFMAN)) return fail(UW_ERR_UNSUPPORTED, "no Huffman stream");
+      bytes = 256; host = f.lengths; break;
+    default:
+      return fail(UW_ERR_INVALID_ARG, "unknown stream %d", which);
+  }
+  *len = bytes;
+  if (!dst || cap < bytes) return fail(UW_ERR_INVALID_ARG, "destination holds %zu bytes, stream needs %zu", cap, bytes);
+  if (bytes == 0) return UW_OK;
+  const bool from_host = h->host_only || which == UW_STREAM_PALETTE || which == UW_STREAM_LENGTHS || tmp.size();
+  if (from_host) {
+    std::memcpy(dst, host, bytes);
+  } else {
+    UW_HIP(hipMemcpy(dst, dev, bytes, hipMemcpyDeviceToHost));
+  }
+  return UW_OK;
+}
+
+uw_status uw_clone(uw_handle h, uw_handle* out) {
+  if (!h || !out) return fail(UW_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
+  uw_matrix* c = new (std::nothrow) uw_matrix;
+  if (!c) return fail(UW_ERR_OOM, "host allocation failed");
+  // scalar fields and the small host tables; the big host streams were released at upload
+  c->hf.rows = h->hf.rows;
+  c->hf.cols = h->hf.cols;
+  c->hf.formats = h->hf.formats;
+  std::memcpy(c->hf.hist, h->hf.hist, sizeof c->hf.hist);
+  c->hf.distinct = h->hf.distinct;
+  std::memcpy(c->hf.palette, h->hf.palette, 16);
+  c->hf.n_raw = h->hf.n_raw;
+  std::memcpy(c->hf.lengths, h->hf.lengths, 256);
+  std::memcpy(c->hf.codes, h->hf.codes, sizeof c->hf.codes);
+  c->hf.stream_bits = h->hf.stream_bits;
+  c->rows = h->rows;
+  c->cols = h->cols;
+  c->formats = h->formats;
+  std::memcpy(c->lut_v, h->lut_v, sizeof c->lut_v);
+  c->words_total = h->words_total;
+  c->plan_n = h->plan_n;
+  std::memcpy(c->plan_tok, h->plan_tok, sizeof c->plan_tok);
+  std::memcpy(c->plan_pipe, h->plan_pipe, sizeof c->plan_pipe);
+  std::memcpy(c->plan_var, h->plan_var, sizeof c->plan_var);
+  c->variant = h->variant;
+  if (hipMalloc(&c->dmem, h->dmem_bytes) != hipSuccess) {
+    delete c;
+    return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", h->dmem_bytes);
+  }
+  c->dmem_bytes = h->dmem_bytes;
+  auto rebase = [&](auto* p) -> decltype(p) {
+    if (!p) return nullptr;
+    const size_t off = reinterpret_cast<const uint8_t*>(p) - static_cast<const uint8_t*>(h->dmem);
+    return reinterpret_cast<decltype(p)>(static_cast<uint8_t*>(c->dmem) + off);
+  };
+  c->d_sm = rebase(h->d_sm);
+  c->d_nib = rebase(h->d_nib);
+  c->d_meta = rebase(h->d_meta);
+  c->d_side = rebase(h->d_side);
+  c->d_code_of = rebase(h->d_code_of);
+  c->d_words = rebase(h->d_words);
+  c->d_offsets = rebase(h->d_offsets);
+  c->d_lut = rebase(h->d_lut);
+  if (hipMemcpy(c->dmem, h->dmem, h->dmem_bytes, hipMemcpyDeviceToDevice) != hipSuccess ||
+      hipEventCreateWithFlags(&c->prep_done, hipEventDisableTiming) != hipSuccess) {
+    (void)hipFree(c->dmem);
+    delete c;
+    return fail(UW_ERR_HIP, "device copy failed");
+  }
+  *out = c;
+  return UW_OK;
+}
+
+void uw_free(uw_handle h) {
+  if (!h) return;
+  if (!h->host_only) {
+    (void)hipDeviceSynchronize();
+    if (h->scratch && h->own_scratch) {
+      scratch_forget(h->scratch);
+      (void)hipFree(h->scratch);
+    }
+    if (h->dmem) (void)hipFree(h->dmem);
+    if (h->prep_done) (void)hipEventDestroy(h->prep_done);
+  }
+  delete h;
+}
+
+uw_status uw_silu_mul(const float* g, const float* u, uint16_t* hh, int64_t n, void* stream) {
+  if (!g || !u || !hh) return fail(UW_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(UW_ERR_INVALID_ARG, "negative size");
+  UW_HIP(uw::launch_silu_mul(g, u, hh, n, static_cast<hipStream_t>(stream)));
+  return UW_OK;
+}
+
+size_t uw_mlp_workspace_bytes(int64_t tokens, int64_t inter) {
+  const size_t t = size_t(std::max<int64_t>(tokens, 0)), i = size_t(std::max<int64_t>(inter, 0));
+  return 2 * align256(t * i * 4) + align256(t * i * 2);
+}
+
+uw_status uw_mlp_forward(uw_handle gate, uw_handle up, uw_handle down, const int32_t* pipelines,
+                         const uint16_t* x_dev, float* y_dev, int64_t tokens, void* work_dev, size_t work_bytes) {
+  if (!gate || !up || !down || !pipelines || !x_dev || !y_dev || !work_dev)
+    return fail(UW_ERR_INVALID_ARG, "null argument");
+  const int64_t inter = gate->rows, hidden = gate->cols;
+  if (up->rows != inter || up->cols != hidden || down->rows != hidden || down->cols != inter)
+    return fail(UW_ERR_SHAPE, "gate/up [inter, hidden] and down [hidden, inter] shapes disagree");
+  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
+  if (work_bytes < uw_mlp_workspace_bytes(tokens, inter)) return fail(UW_ERR_INVALID_ARG, "workspace too small");
+  uint8_t* cur = static_cast<uint8_t*>(work_dev);
+  float* g = carve<float>(cur, size_t(tokens) * inter * 4);
+  float* u = carve<float>(cur, size_t(tokens) * inter * 4);
+  uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
+  uw_status st;
+  if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
+  if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;
+  UW_HIP(uw::launch_silu_mul(g, u, hh, tokens * inter, gate->main));
+  return matmul_impl(down, hh, y_dev, tokens, pipelines[2]);
+}
+
+size_t uw_stack_workspace_bytes(int64_t tokens, int64_t hidden, int64_t inter) {
+  const size_t t = size_t(std::max<int64_t>(tokens, 0)), hd = size_t(std::max<int64_t>(hidden, 0));
+  return uw_mlp_workspace_bytes(tokens, inter) + align256(t * hd * 4) + align256(t * hd * 2);
+}
+
+uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, int32_t layers,
+                           const uint16_t* x_dev, float* y_dev, int64_t tokens, int32_t overlap, void* work_dev,
+                           size_t work_bytes) {
+  if (!handles || !pipelines || !x_dev || !y_dev || !work_dev || layers < 1)
+    return fail(UW_ERR_INVALID_ARG, "bad argument");
+  const int64_t inter = handles[0]->rows, hidden = handles[0]->cols;
+  if (work_bytes < uw_stack_workspace_bytes(tokens, hidden, inter))
+    return fail(UW_ERR_INVALID_ARG, "workspace too small");
+  const size_t mlp_ws = uw_mlp_workspace_bytes(tokens, inter);
+  uint8_t* cur = static_cast<uint8_t*>(work_dev) + mlp_ws;
+  float* ytmp = carve<float>(cur, size_t(tokens) * hidden * 4);
+  uint16_t* xnext = carve<uint16_t>(cur, size_t(tokens) * hidden * 2);
+  hipStream_t main = handles[0]->main;
+  auto hard = [&](int l, int j, int* p) {
+    int var = 0;
+    *p = resolve_pipeline(handles[3 * l + j], tokens, pipelines[3 * l + j], &var);
+    return *p >= 1 && *p <= 3;
+  };
+  auto issue_prep = [&](int l) -> uw_status {
+    for (int j = 0; j < 3; ++j) {
+      int p = 0;
+      if (hard(l, j, &p)) {
+        uw_status st = uw_preprocess(handles[3 * l + j], p);
+        if (st != UW_OK) return st;
+      }
+    }
+    return UW_OK;
+  };
+  uw_status st;
+  if (overlap && (st = issue_prep(0)) != UW_OK) return st;
+  const uint16_t* xin = x_dev;
+  for (int l = 0; l < layers; ++l) {
+    if (handles[3 * l]->main != main) return fail(UW_ERR_INVALID_ARG, "all handles must share one main stream");
+    if (overlap && l + 1 < layers && (st = issue_prep(l + 1)) != UW_OK) return st;
+    int32_t p3[3];
+    for (int j = 0; j < 3; ++j) {
+      int var = 0;
+      p3[j] = resolve_pipeline(handles[3 * l + j], tokens, pipelines[3 * l + j], &var);
+    }
+    float* yout = l + 1 == layers ? y_dev : ytmp;
+    if ((st = uw_mlp_forward(handles[3 * l], handles[3 * l + 1], handles[3 * l + 2], p3, xin, yout, tokens,
+                             work_dev, mlp_ws)) != UW_OK)
+      return st;
+    if (l + 1 < layers) {
+      UW_HIP(uw::launch_f32_to_bf16(yout, xnext, tokens * hidden, main));
+      xin = xnext;
+    }
+  }
+  return UW_OK;
+}
+
+uw_status uw_stream_create(int32_t cu_first, int32_t cu_count, void** out) {
+  if (!out) return fail(UW_ERR_INVALID_ARG, "null output");
+  int dev = 0;
+  UW_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  UW_HIP(hipGetDeviceProperties(&prop, dev));
+  const int ncu = prop.multiProcessorCount;
+  if (cu_first < 0 || cu_count < 1 || cu_first + cu_count > ncu)
+    return fail(UW_ERR_INVALID_ARG, "CU range [%d, %d) outside 0..%d", cu_first, cu_first + cu_count, ncu);
+  std::vector<uint32_t> mask((ncu + 31) / 32, 0u);
+  for (int c = cu_first; c < cu_first + cu_count; ++c) mask[c / 32] |= 1u << (c % 32);
+  hipStream_t s = nullptr;
+  UW_HIP(hipExtStreamCreateWithCUMask(&s, (uint32_t)mask.size(), mask.data()));
+  *out = s;
+  return UW_OK;
+}
+
+uw_status uw_stream_destroy(void* stream) {
+  if (!stream) return fail(UW_ERR_INVALID_ARG, "null stream");
+  UW_HIP(hipStreamDestroy(static_cast<hipStream_t>(stream)));
+  return UW_OK;
+}
+
+int32_t uw_device_cu_count(void) {
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  return prop.multiProcessorCount;
+}
+
+uw_status uw_gemm_bf16(const uint16_t* x_dev, const uint16_t* w_dev, float* y_dev, int64_t tokens, int64_t rows,
+                       int64_t cols, void* stream) {
+  if (!x_dev || !w_dev || !y_dev) return fail(UW_ERR_INVALID_ARG, "null pointer");
+  if (tokens < 1 || rows < 1 || cols < 1) return fail(UW_ERR_SHAPE, "bad shape");
+  return gemm_bf16(x_dev, w_dev, y_dev, tokens, rows, cols, static_cast<hipStream_t>(stream));
+}
+
+uw_status uw_device_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(UW_ERR_INVALID_ARG, "null pointer");
+  if (bytes % 16) return fail(UW_ERR_INVALID_ARG, "size must be a multiple of 16");
+  UW_HIP(uw::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+  return UW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Fused-kernel variants: the kernel shapes the autotuner chooses from
+// (Unweight page, section 九: pipeline x kernel variant x decode/compute split).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace uw {
+
+hipError_t launch_fused_small(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                              hipStream_t s);
+hipError_t launch_fused_large(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                              hipStream_t s);
+
+namespace {
+
+struct Named {
+  Variant v;
+  const char* name;
+};
+
+// small batch: kind 0, {waves, ksplit, unroll}
+const Named kSmall[] = {
+    {{0, 8, 1, 2, 0}, "small:w8:k1:u2"},  {{0, 4, 1, 2, 0}, "small:w4:k1:u2"},
+    {{0, 16, 1, 1, 0}, "small:w16:k1:u1"}, {{0, 8, 1, 4, 0}, "small:w8:k1:u4"},
+    {{0, 4, 1, 4, 0}, "small:w4:k1:u4"},  {{0, 8, 2, 2, 0}, "small:w8:k2:u2"},
+    {{0, 8, 4, 2, 0}, "small:w8:k4:u2"},  {{0, 4, 2, 2, 0}, "small:w4:k2:u2"},
+    {{0, 16, 1, 2, 0}, "small:w16:k1:u2"}, {{0, 4, 4, 2, 0}, "small:w4:k4:u2"},
+    {{0, 8, 1, 1, 0}, "small:w8:k1:u1"},  {{0, 4, 4, 4, 0}, "small:w4:k4:u4"},
+};
+// large batch: kind 1, {tile, ksplit}
+const Named kLarge[] = {
+    {{1, 0, 1, 0, 0}, "large:t0(4x64r x128t):k1"}, {{1, 0, 2, 0, 0}, "large:t0(4x64r x128t):k2"},
+    {{1, 0, 4, 0, 0}, "large:t0(4x64r x128t):k4"}, {{1, 0, 1, 0, 1}, "large:t1(4x32r x128t):k1"},
+    {{1, 0, 2, 0, 1}, "large:t1(4x32r x128t):k2"}, {{1, 0, 1, 0, 2}, "large:t2(2x64r x128t):k1"},
+    {{1, 0, 2, 0, 2}, "large:t2(2x64r x128t):k2"}, {{1, 0, 1, 0, 3}, "large:t3(4x64r x64t):k1"},
+    {{1, 0, 2, 0, 3}, "large:t3(4x64r x64t):k2"},
+};
+constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
+constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
+
+}  // namespace
+
+int variant_count(int64_t tokens) { return 1 + (tokens <= 64 ? kNSmall : kNLarge); }
+
+bool variant_get(int64_t tokens, int id, Variant* v) {
+  if (id < 1 || id >= variant_count(tokens)) return false;
+  *v = tokens <= 64 ? kSmall[id - 1].v : kLarge[id - 1].v;
+  return true;
+}
+
+const char* variant_name(int64_t tokens, int id) {
+  if (id == 0) return tokens <= 64 ? "small:default" : "large:default";
+  if (id < 0 || id >= variant_count(tokens)) return nullptr;
+  return tokens <= 64 ? kSmall[id - 1].name : kLarge[id - 1].name;
+}
+
+Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
+  const int64_t brows = rows / 16, kbn = cols / 64;
+  if (tokens <= 64) {
+    Variant v{0, 8, 1, 2, 0};
+    if (brows < 512) v.ksplit = (int)std::min<int64_t>({4, (1024 + brows - 1) / brows, kbn});
+    return v;
+  }
+  Variant v{1, 0, 1, 0, 0};
+  const int64_t wgs = ((brows + 15) / 16) * ((tokens + 127) / 128);
+  if (wgs < 512) v.ksplit = (int)std::min<int64_t>({4, (512 + wgs - 1) / wgs, kbn});
+  return v;
+}
+
+hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v0,
+                        hipStream_t s) {
+  Variant v = v0;
+  v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, w.cols / 64));
+  if (tokens <= 64) {
+    if (v.kind != 0) return hipErrorInvalidValue;
+    return launch_fused_small(w, x, y, tokens, v, s);
+  }
+  if (v.kind != 1) return hipErrorInvalidValue;
+  return launch_fused_large(w, x, y, tokens, v, s);
+}
+
+}  // namespace uw

@@ -1,0 +1,235 @@
+/*
+ * uw.h -- C ABI of a lossless BF16 weight codec with fused decode-into-matmul
+ * kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one described on the page "Unweight: how Cloudflare
+ * compresses large models by 22% without losing precision":
+ *   section 三  BF16 = 1 sign + 8 exponent + 7 mantissa bits; the exponent byte
+ *               is the redundant part;
+ *   section 四  Huffman code on the exponent bytes only, sign+mantissa kept
+ *               verbatim; a palette of the 16 most frequent exponents; a row of
+ *               64 weights holding any other exponent is stored raw;
+ *   section 五  decompress on chip, never write the rebuilt weights to HBM;
+ *   section 六  four execution pipelines (full decode + library GEMM,
+ *               exponent-only decode, runtime palette transcode, direct palette);
+ *   section 七  the reconstructing matmul;
+ *   section 八  hard (Huffman) and easy (palette) layers, the next hard layer
+ *               decoded on a side stream while an easy layer computes;
+ *   section 九  an autotuner choosing the pipeline and decode/compute CU split.
+ *
+ * Conventions (all entry points):
+ *   - Matrices are row-major.  A weight matrix W is [rows, cols] = [out, in]
+ *     (a linear layer's weight), bf16 passed as uint16_t bit patterns.
+ *     rows must be a multiple of 16 and cols a multiple of 64.
+ *   - Activations X are [tokens, cols] bf16 (uint16_t), contiguous, on the
+ *     device.  Outputs Y are [tokens, rows] float32, contiguous, on the device,
+ *     overwritten (Y = X * W^T).
+ *   - Pointers named *_host are host memory, *_dev device memory (hipMalloc or
+ *     a torch CUDA tensor).  The caller owns every pointer it passes; the
+ *     library only reads host inputs during the call.
+ *   - Device work is enqueued on the handle's main stream (default: the null
+ *     stream) and the call returns without synchronising.  Results are valid
+ *     once that stream is synchronised.  Launch errors come back as
+ *     UW_ERR_HIP; a device fault surfaces on a later call.
+ *   - Every call returns a uw_status; on failure uw_last_error() gives a
+ *     message (thread-local).  No C++ exception crosses this boundary.
+ *   - A handle is not safe for concurrent use from several host threads.
+ */
+#ifndef UW_H
+#define UW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct uw_matrix* uw_handle;
+
+typedef enum {
+  UW_OK = 0,
+  UW_ERR_INVALID_ARG = 1,   /* null pointer, bad enum, tokens <= 0 ...        */
+  UW_ERR_SHAPE = 2,         /* rows % 16 != 0, cols % 64 != 0, size overflow  */
+  UW_ERR_OOM = 3,           /* host or device allocation failed               */
+  UW_ERR_HIP = 4,           /* a HIP / hipBLASLt call failed                  */
+  UW_ERR_FORMAT = 5,        /* stream too long for 32-bit offsets, bad table  */
+  UW_ERR_UNSUPPORTED = 6,   /* pipeline needs a format the handle lacks, or a
+                               device call on a host-only handle              */
+  UW_ERR_NO_DEVICE = 7      /* no gfx950 device visible                       */
+} uw_status;
+
+/* Section 六: the four pipelines.  UW_P_AUTO picks from the plan set with
+ * uw_set_plan (else a built-in rule: direct palette when the handle has it,
+ * else runtime palette transcode, else full decode). */
+typedef enum {
+  UW_P_AUTO = 0,
+  UW_P1_FULL_DECODE = 1,       /* Huffman -> bf16 W in scratch, then hipBLASLt     */
+  UW_P2_EXP_DECODE = 2,        /* Huffman -> exponent bytes in scratch, fused GEMM */
+  UW_P3_PALETTE_TRANSCODE = 3, /* Huffman -> 4-bit codes in scratch, fused GEMM    */
+  UW_P4_DIRECT_PALETTE = 4     /* resident 4-bit codes, fused GEMM, no preprocess  */
+} uw_pipeline;
+
+/* Format flags for uw_encode (section 四, section 六). */
+#define UW_FMT_HUFFMAN   0x1u   /* Huffman exponent stream + chunk bit offsets     */
+#define UW_FMT_PALETTE   0x2u   /* 4-bit codes + raw-group tables (direct palette) */
+#define UW_FMT_RAWAUX    0x4u   /* only the palette and raw-group tables: lets a
+                                   Huffman matrix run pipeline 3                   */
+#define UW_ENC_HOST_ONLY 0x100u /* encode on the host and keep the streams there;
+                                   no device is touched (inspection, export)       */
+
+/* Streams of the stored format, for uw_export.  All per-weight streams are in
+ * the serial order: 16x64 bricks, brick-rows top to bottom, bricks left to
+ * right; inside a brick 64 runs of 16 weights, run l = row l%16, columns
+ * 16*(l/16) .. +15. */
+typedef enum {
+  UW_STREAM_SM = 0,          /* uint8 [rows*cols] sign+mantissa bytes            */
+  UW_STREAM_NIBBLES = 1,     /* uint8 [rows*cols/2] 4-bit codes: of 8 serial
+                                codes, byte b = code b | code b+4 << 4           */
+  UW_STREAM_RAWMAP = 2,      /* uint32 [bricks] bit r = row r's group raw        */
+  UW_STREAM_RAWBEFORE = 3,   /* uint32 [bricks] raw groups in earlier bricks     */
+  UW_STREAM_SIDE = 4,        /* uint8 [raw groups * 64] original exponent bytes  */
+  UW_STREAM_WORDS = 5,       /* uint32 Huffman bitstream, MSB-first per word     */
+  UW_STREAM_OFFSETS = 6,     /* uint32 [chunks] first bit of each 256-symbol chunk */
+  UW_STREAM_PALETTE = 7,     /* uint8 [16] palette, index = 4-bit code           */
+  UW_STREAM_LENGTHS = 8      /* uint8 [256] Huffman code length per exponent     */
+} uw_stream;
+
+typedef struct {
+  int64_t rows, cols;
+  uint32_t formats;            /* UW_FMT_* resident in this handle              */
+  uint32_t chunk;              /* Huffman symbols per chunk (256)               */
+  uint32_t lmax;               /* longest Huffman code (12)                     */
+  uint32_t distinct_exponents;
+  uint8_t palette[16];
+  uint8_t code_lengths[256];
+  uint64_t raw_groups, groups;
+  uint64_t stream_bits;        /* Huffman payload bits (without padding)        */
+  uint64_t stream_words;       /* payload words (without the 4 padding words)   */
+  double bpw_palette;          /* bits/weight of the direct-palette form        */
+  double bpw_huffman;          /* bits/weight of the Huffman form               */
+  double bpw_resident;         /* bits/weight of what this handle stores        */
+  uint64_t resident_bytes;     /* compressed bytes held on the device           */
+  uint64_t scratch_bytes[5];   /* scratch that pipeline p (1..4) needs          */
+} uw_info;
+
+/* Encode a bf16 matrix (section 四): split each weight into its exponent and
+ * sign+mantissa bytes, build the formats requested in `formats` and upload them
+ * to the current HIP device (unless UW_ENC_HOST_ONLY).  w_host: [rows, cols]
+ * host array, read only during the call.  *out receives a new handle to free
+ * with uw_free.  UW_ERR_SHAPE on bad shape, UW_ERR_FORMAT if the Huffman
+ * stream exceeds 2^32 bits. */
+uw_status uw_encode(const uint16_t* w_host, int64_t rows, int64_t cols, uint32_t formats,
+                    uw_handle* out);
+
+/* Rebuild the original bf16 matrix on the device (section 十: bit-exact).
+ * Uses the GPU Huffman decoder when the handle holds UW_FMT_HUFFMAN, else the
+ * palette form.  w_dev_out: [rows, cols] uint16 device buffer. */
+uw_status uw_decode(uw_handle h, uint16_t* w_dev_out);
+
+/* Y[tokens, rows] = X[tokens, cols] * W^T through `pipeline` (section 六, 七).
+ * x_dev, y_dev: device buffers as in the conventions.  tokens >= 1.
+ * Pipelines 1-3 need UW_FMT_HUFFMAN (3 also PALETTE or RAWAUX), 4 needs
+ * UW_FMT_PALETTE, else UW_ERR_UNSUPPORTED.  Pipelines 1-3 first run their
+ * preprocessing into the handle's scratch unless uw_preprocess already queued
+ * it, in which case the main stream waits for that work. */
+uw_status uw_matmul(uw_handle h, const uint16_t* x_dev, float* y_dev, int64_t tokens, int pipeline);
+
+/* Section 八: enqueue the preprocessing of `pipeline` (1-3) on the handle's
+ * side stream, writing the handle's scratch, and record an event that the next
+ * uw_matmul with the same pipeline waits on.  Returns UW_ERR_UNSUPPORTED for
+ * pipeline 4 or a missing format. */
+uw_status uw_preprocess(uw_handle h, int pipeline);
+
+/* Streams (hipStream_t passed as void*; NULL = the null stream).  The side
+ * stream defaults to the main stream. */
+uw_status uw_set_streams(uw_handle h, void* main_stream, void* side_stream);
+
+/* Caller-owned device scratch for pipelines 1-3 (at least
+ * uw_info.scratch_bytes[p] bytes, 256-byte aligned).  Without it the handle
+ * allocates its own on first use.  Several handles may share one buffer when
+ * their use does not overlap in time. */
+uw_status uw_set_scratch(uw_handle h, void* scratch_dev, size_t bytes);
+
+/* Autotuner output (section 九): for UW_P_AUTO, the first entry with
+ * tokens <= max_tokens[i] selects pipeline[i] and kernel variant[i]
+ * (variant 0 = built-in choice).  n <= 16; n = 0 clears the plan. */
+uw_status uw_set_plan(uw_handle h, const int32_t* max_tokens, const int32_t* pipeline,
+                      const int32_t* variant, int32_t n);
+
+/* Force the fused-kernel variant for explicit pipelines (0 = built-in choice).
+ * Variants are listed by uw_variant_name. */
+uw_status uw_set_variant(uw_handle h, int32_t variant);
+
+/* Name of fused-kernel variant `variant` for `tokens`, or NULL past the end. */
+const char* uw_variant_name(int64_t tokens, int32_t variant);
+
+uw_status uw_query(uw_handle h, uw_info* out);
+
+/* Copy one stored stream to host memory `dst` (capacity `cap` bytes);
+ * *len receives its size in bytes (set even when dst is NULL or too small,
+ * in which case UW_ERR_INVALID_ARG is returned). */
+uw_status uw_export(uw_handle h, int which, void* dst, size_t cap, size_t* len);
+
+/* A new handle holding a device copy of h's resident streams (same formats,
+ * plan and variant; own scratch, default streams).  Used to place copies of
+ * one matrix at distinct addresses, e.g. to rotate weight copies past the
+ * 256 MB Infinity Cache when measuring HBM throughput. */
+uw_status uw_clone(uw_handle h, uw_handle* out);
+
+void uw_free(uw_handle h);
+
+const char* uw_last_error(void);
+
+/* ---- SwiGLU glue and the layer pipeline (section 八, section 十一) ---- */
+
+/* h_dev[i] = bf16(silu(g_dev[i]) * u_dev[i]), silu(g) = g / (1 + exp(-g)),
+ * float32 arithmetic, round to nearest even.  n elements, on `stream`. */
+uw_status uw_silu_mul(const float* g_dev, const float* u_dev, uint16_t* h_dev, int64_t n, void* stream);
+
+/* One SwiGLU MLP layer y = down(silu(gate x) * up x) with the projections
+ * given as handles (gate/up [inter, hidden], down [hidden, inter]).
+ * pipelines[3] selects each projection's pipeline (UW_P_AUTO allowed).
+ * work_dev: at least uw_mlp_workspace_bytes(tokens, inter) bytes of device
+ * memory for the gate/up outputs and h.  Runs on gate's main stream. */
+uw_status uw_mlp_forward(uw_handle gate, uw_handle up, uw_handle down, const int32_t* pipelines,
+                         const uint16_t* x_dev, float* y_dev, int64_t tokens, void* work_dev,
+                         size_t work_bytes);
+size_t uw_mlp_workspace_bytes(int64_t tokens, int64_t inter);
+
+/* A stack of MLP layers (section 八): layer l uses handles[3l .. 3l+2]
+ * (gate, up, down) and pipelines[3l .. 3l+2].  Each layer's input is the
+ * previous layer's output rounded to bf16; y_dev gets the last layer's output.
+ * With overlap != 0, the preprocessing of every hard projection (pipeline
+ * 1-3) is issued on its handle's side stream one layer ahead, while the
+ * previous layer computes; handles of consecutive layers must then not share
+ * scratch.  work_dev: uw_stack_workspace_bytes(tokens, hidden, inter) bytes. */
+uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, int32_t layers,
+                           const uint16_t* x_dev, float* y_dev, int64_t tokens, int32_t overlap,
+                           void* work_dev, size_t work_bytes);
+size_t uw_stack_workspace_bytes(int64_t tokens, int64_t hidden, int64_t inter);
+
+/* ---- Streams with a CU mask (section 九's decode/compute split) ---- */
+
+/* Create a stream limited to compute units [cu_first, cu_first + cu_count)
+ * of the current device (default priority).  *out receives a hipStream_t. */
+uw_status uw_stream_create(int32_t cu_first, int32_t cu_count, void** out);
+uw_status uw_stream_destroy(void* stream);
+int32_t uw_device_cu_count(void);
+
+/* ---- Reference points for measurement ---- */
+
+/* Uncompressed baseline: y[tokens, rows] = x * w^T with w_dev a plain bf16
+ * [rows, cols] matrix, through hipBLASLt (the library GEMM of pipeline 1). */
+uw_status uw_gemm_bf16(const uint16_t* x_dev, const uint16_t* w_dev, float* y_dev, int64_t tokens,
+                       int64_t rows, int64_t cols, void* stream);
+
+/* Plain device copy of `bytes` bytes (multiple of 16) with 16-byte loads and
+ * stores: the measured HBM ceiling. */
+uw_status uw_device_copy(const void* src_dev, void* dst_dev, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UW_H */

@@ -1,0 +1,301 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bar (from the method): decoded weights and every intermediate stream
+(exponent bytes, 4-bit codes) bit-exact; matmul outputs within
+max|gpu - ref| / max|ref| <= 1e-3 of the fp64 oracle; one-hot activations
+reproduce weights exactly (an fp32 sum of one exact product).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import decode_gemm_bf16_amd as uw
+    return torch, uw
+
+
+def _dev_x(env, x_bits):
+    torch, uw = env
+    return uw.bf16_tensor(x_bits)
+
+
+def _run(env, m, x_bits, pipeline, variant=0):
+    torch, uw = env
+    x = uw.bf16_tensor(x_bits)
+    y = torch.full((x_bits.shape[0], m.rows), float("nan"), device="cuda", dtype=torch.float32)
+    m.set_variant(variant)
+    m.matmul(x, y, pipeline=pipeline)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _both(env, w):
+    torch, uw = env
+    return uw.Matrix(w, uw.FMT_HUFFMAN | uw.FMT_PALETTE)
+
+
+def test_mfma_fragment_layout_one_hot(env):
+    """One-hot activations: Y[m, n] == W[n, k_m] exactly for every pipeline and
+    small/large batch (checks reconstruction and the MFMA output layout)."""
+    torch, uw = env
+    w = synth.weights(48, 256, 11, 0.01, 12)
+    m = _both(env, w)
+    ref_bits = w
+    for tokens in (1, 5, 16, 17, 64, 65, 130):
+        x, ks = synth.one_hot_activations(tokens, 256, seed=tokens)
+        for p in (1, 2, 3, 4):
+            y = _run(env, m, x, p)
+            want = synth.bf16_bits_to_f32(ref_bits[:, ks].T.copy())
+            assert np.array_equal(y, want), (tokens, p)
+
+
+@pytest.mark.parametrize("name", ["tiny", "patterns", "ragged"])
+def test_decode_bit_exact(env, name):
+    torch, uw = env
+    if name == "tiny":
+        c = synth.CONFIGS["tiny"]
+        w = synth.weights(c["rows"], c["cols"], c["seed"], c["p"], c["shift"])
+    elif name == "patterns":
+        w = synth.all_bf16_patterns()
+    else:
+        w = synth.weights(272, 576, 3, 0.003, 12)
+    for fmt in (uw.FMT_HUFFMAN, uw.FMT_PALETTE, uw.FMT_HUFFMAN | uw.FMT_PALETTE):
+        m = uw.Matrix(w, fmt)
+        out = torch.empty(w.shape, dtype=torch.int16, device="cuda")
+        m.decode(out)
+        torch.cuda.synchronize()
+        assert np.array_equal(uw.bits_of(out), w), fmt
+
+
+def test_preprocess_streams_bit_exact(env):
+    """Pipeline 2's exponent bytes and pipeline 3's 4-bit codes equal the oracle's."""
+    torch, uw = env
+    w = synth.weights(272, 576, 5, 0.004, 12)
+    m = _both(env, w)
+    inf = m.info()
+    e_serial = oracle.to_serial(oracle.split(w)[0])
+    pe = oracle.palette_encode(w)
+    for p, want in ((2, e_serial), (3, pe["nibbles"]), (1, w)):
+        buf = torch.empty(inf["scratch_bytes"][p], dtype=torch.uint8, device="cuda")
+        m.set_scratch(buf)
+        m.preprocess(p)
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        if p == 1:
+            got = got[: w.size * 2].view(np.uint16).reshape(w.shape)
+        else:
+            got = got[: want.size]
+        assert np.array_equal(got, want), p
+    # the resident palette codes uploaded by the encoder, read back from the device
+    assert np.array_equal(m.export(uw.STREAM_NIBBLES), pe["nibbles"])
+
+
+@pytest.mark.parametrize("shape", [(256, 512), (272, 576), (48, 4096)])
+@pytest.mark.parametrize("tokens", [1, 3, 16, 33, 64, 65, 129, 300])
+def test_matmul_random_all_pipelines(env, shape, tokens):
+    torch, uw = env
+    rows, cols = shape
+    w = synth.weights(rows, cols, 0, 0.001, 12)
+    x = synth.activations(tokens, cols, xseed=1)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    for p in (1, 2, 3, 4):
+        y = _run(env, m, x, p)
+        assert np.isfinite(y).all(), p
+        assert oracle.rel_err(y, ref) <= TOL, (p, oracle.rel_err(y, ref))
+
+
+@pytest.mark.parametrize("tokens", [1, 16, 64, 100, 256])
+def test_every_variant(env, tokens):
+    torch, uw = env
+    w = synth.weights(528, 1024, 2, 0.002, 12)
+    x = synth.activations(tokens, 1024, xseed=3)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    names = uw.variants(tokens)
+    for v in range(len(names)):
+        for p in (2, 4):
+            y = _run(env, m, x, p, variant=v)
+            assert oracle.rel_err(y, ref) <= TOL, (names[v], p)
+
+
+def test_gate_full_size_batch1(env):
+    """14336x4096 gate, batch 1 (the headline workload): full decode bit-exact,
+    resident codes bit-exact, sampled outputs of all pipelines vs fp64."""
+    torch, uw = env
+    c = synth.CONFIGS["gate_8b"]
+    w = synth.weights(c["rows"], c["cols"], c["seed"], c["p"], c["shift"])
+    m = _both(env, w)
+    out = torch.empty(w.shape, dtype=torch.int16, device="cuda")
+    m.decode(out)
+    torch.cuda.synchronize()
+    assert np.array_equal(uw.bits_of(out), w)
+    del out
+    x = synth.activations(1, c["cols"], xseed=c["xseed"])
+    rows = np.random.default_rng(0).choice(c["rows"], 512, replace=False)
+    ref = oracle.matmul_fp64_rows(x, w, rows)
+    ys = {}
+    for p in (1, 2, 3, 4):
+        ys[p] = _run(env, m, x, p)
+        assert oracle.rel_err(ys[p][:, rows], ref) <= TOL, p
+    for p in (1, 2, 3):
+        assert oracle.rel_err(ys[p], ys[4]) <= TOL, p
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_mlp_8b_shapes_sampled(env, proj):
+    torch, uw = env
+    c = synth.CONFIGS["mlp_8b"]
+    rows, cols, seed = c[proj]
+    w = synth.weights(rows, cols, seed, c["p"], c["shift"])
+    m = _both(env, w)
+    sample = np.random.default_rng(1).choice(rows, 256, replace=False)
+    xs = synth.activations(1024, cols, xseed=1)
+    for tokens in (1, 16, 64, 256, 1024):
+        x = xs[:tokens]
+        ref = oracle.matmul_fp64_rows(x, w, sample)
+        for p in (1, 2, 3, 4):
+            y = _run(env, m, x, p)
+            assert oracle.rel_err(y[:, sample], ref) <= TOL, (tokens, p)
+
+
+def test_silu_mul(env):
+    torch, uw = env
+    rng = np.random.default_rng(4)
+    g = (rng.standard_normal(10003) * 3).astype(np.float32)
+    u = rng.standard_normal(10003).astype(np.float32)
+    gd, ud = torch.from_numpy(g).cuda(), torch.from_numpy(u).cuda()
+    h = torch.empty(10003, dtype=torch.int16, device="cuda")
+    uw.silu_mul(gd, ud, h)
+    torch.cuda.synchronize()
+    got = oracle.bf16_to_f64(uw.bits_of(h))
+    want = oracle.bf16_to_f64(oracle.silu_mul_bf16(g.astype(np.float64), u.astype(np.float64)))
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30)
+
+
+def test_mlp_layer_and_stack(env):
+    torch, uw = env
+    hidden, inter, tokens = 256, 512, 9
+    ws = [synth.weights(inter, hidden, 20, 0.002, 10), synth.weights(inter, hidden, 21, 0.002, 10),
+          synth.weights(hidden, inter, 22, 0.002, 10)]
+    x = synth.activations(tokens, hidden, xseed=5)
+    _, _, _, ref = oracle.mlp_layer_fp64(x, *ws)
+    mats = [_both(env, w) for w in ws]
+    xd = uw.bf16_tensor(x)
+    y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+    work = torch.empty(uw.mlp_workspace_bytes(tokens, inter), dtype=torch.uint8, device="cuda")
+    for pipes in ([4, 4, 4], [1, 2, 3], [3, 3, 2]):
+        uw.mlp_forward(*mats, pipes, xd, y, tokens, work)
+        torch.cuda.synchronize()
+        assert oracle.rel_err(y.cpu().numpy(), ref) <= 2 * TOL, pipes
+    # a 4-layer stack, alternating hard (Huffman) and easy (palette) layers
+    L = 4
+    # std 0.05 and no outliers keep activations of an un-normalised stack in range
+    layer_w = [[synth.weights(inter, hidden, 100 + 3 * l, 0.0, 0, std=0.05),
+                synth.weights(inter, hidden, 101 + 3 * l, 0.0, 0, std=0.05),
+                synth.weights(hidden, inter, 102 + 3 * l, 0.0, 0, std=0.05)] for l in range(L)]
+    xin = x
+    for l in range(L):
+        _, _, _, yl = oracle.mlp_layer_fp64(xin, *layer_w[l])
+        xin = oracle.f64_to_bf16_rne(yl)
+    ref_stack = yl
+    side = torch.cuda.Stream()
+    stack = []
+    pipes = []
+    scratch = [[torch.empty(2 * inter * hidden, dtype=torch.uint8, device="cuda") for _ in range(3)] for _ in range(2)]
+    for l in range(L):
+        for j in range(3):
+            m = _both(env, layer_w[l][j])
+            m.set_streams(torch.cuda.current_stream(), side)
+            m.set_scratch(scratch[l % 2][j])
+            stack.append(m)
+            pipes.append(3 if l % 2 == 0 else 4)
+    work = torch.empty(uw.stack_workspace_bytes(tokens, hidden, inter), dtype=torch.uint8, device="cuda")
+    outs = []
+    for overlap in (False, True, True):
+        ys = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        uw.stack_forward(stack, pipes, xd, ys, tokens, work, overlap=overlap)
+        torch.cuda.synchronize()
+        outs.append(ys.cpu().numpy())
+        assert oracle.rel_err(outs[-1], ref_stack) <= 5 * TOL, overlap
+    assert np.array_equal(outs[1], outs[2])
+
+
+def test_gemm_baseline_and_copy(env):
+    torch, uw = env
+    w = synth.weights(512, 1024, 7, 0.0, 0)
+    x = synth.activations(37, 1024, xseed=2)
+    y = torch.empty((37, 512), device="cuda", dtype=torch.float32)
+    uw.gemm_bf16(uw.bf16_tensor(x), uw.bf16_tensor(w), y, 37, 512, 1024)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y.cpu().numpy(), oracle.matmul_fp64(x, w)) <= TOL
+    src = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    uw.device_copy(src, dst, src.numel() * 4)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+def test_device_error_paths(env):
+    torch, uw = env
+    w = synth.weights(32, 128, 1, 0.0, 0)
+    x = uw.bf16_tensor(synth.activations(2, 128))
+    y = torch.empty((2, 32), device="cuda", dtype=torch.float32)
+    mh = uw.Matrix(w, uw.FMT_HUFFMAN)
+    with pytest.raises(uw.UwError) as e:
+        mh.matmul(x, y, pipeline=uw.P4_DIRECT_PALETTE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        mh.matmul(x, y, pipeline=uw.P3_PALETTE_TRANSCODE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        mh.matmul(x, y, tokens=0)
+    assert e.value.status == uw.ERR_INVALID_ARG
+    mp = uw.Matrix(w, uw.FMT_PALETTE)
+    with pytest.raises(uw.UwError) as e:
+        mp.preprocess(uw.P1_FULL_DECODE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        mh.set_scratch(torch.empty(16, dtype=torch.uint8, device="cuda"))
+        mh.matmul(x, y, pipeline=uw.P1_FULL_DECODE)
+    assert e.value.status == uw.ERR_INVALID_ARG
+    # auto pipeline with a plan
+    mb = uw.Matrix(w, uw.FMT_HUFFMAN | uw.FMT_PALETTE)
+    mb.set_plan([(1, 1, 0), (64, 4, 0), (1 << 20, 2, 0)])
+    for t in (1, 2, 70):
+        xt = uw.bf16_tensor(synth.activations(t, 128))
+        yt = torch.empty((t, 32), device="cuda", dtype=torch.float32)
+        mb.matmul(xt, yt)
+        torch.cuda.synchronize()
+        assert oracle.rel_err(yt.cpu().numpy(), oracle.matmul_fp64(synth.activations(t, 128), w)) <= TOL
+
+
+def test_cu_masked_streams(env):
+    torch, uw = env
+    n = uw.device_cu_count()
+    assert n >= 8
+    s1 = uw.stream_create(0, n // 4)
+    s2 = uw.stream_create(n // 4, n - n // 4)
+    w = synth.weights(64, 256, 9, 0.002, 12)
+    x = synth.activations(4, 256)
+    m = _both(env, w)
+    m.set_streams(s2, s1)
+    xd = uw.bf16_tensor(x)
+    y = torch.empty((4, 64), device="cuda", dtype=torch.float32)
+    m.preprocess(3)
+    m.matmul(xd, y, pipeline=3)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(y.cpu().numpy(), oracle.matmul_fp64(x, w)) <= TOL
+    m.free()
+    uw.stream_destroy(s1)
+    uw.stream_destroy(s2)

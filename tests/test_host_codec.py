@@ -1,0 +1,138 @@
+"""The C++ host encoder against the oracle, byte for byte (CPU only).
+
+Host-only handles (UW_ENC_HOST_ONLY) run the library's encoder without touching
+a device; every stored stream is exported and compared with the oracle's.
+Also: every symbol declared in include/uw.h is exported by libuw.so, and the
+host-side argument checks return the documented status codes.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_gemm_bf16_amd as uw
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HOST_ALL = uw.FMT_HUFFMAN | uw.FMT_PALETTE | uw.ENC_HOST_ONLY
+
+
+def test_header_symbols_exported():
+    hdr = open(os.path.join(ROOT, "include", "uw.h")).read()
+    declared = set(re.findall(r"\b(uw_[a-z0-9_]+)\s*\(", hdr))
+    assert declared, "no declarations found"
+    lib = C.CDLL(uw.LIB_PATH)
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+    assert declared == set(uw.EXPORTED)
+
+
+def _compare(w, formats=HOST_ALL):
+    m = uw.Matrix(w, formats)
+    pe = oracle.palette_encode(w)
+    he = oracle.huffman_encode(w)
+    info = m.info()
+    assert np.array_equal(m.export(uw.STREAM_SM), pe["sm"])
+    if formats & uw.FMT_PALETTE:
+        assert np.array_equal(m.export(uw.STREAM_PALETTE), pe["palette"])
+        assert np.array_equal(m.export(uw.STREAM_NIBBLES), pe["nibbles"])
+    if formats & (uw.FMT_PALETTE | uw.FMT_RAWAUX):
+        assert np.array_equal(m.export(uw.STREAM_RAWMAP), pe["brick_rawmap"])
+        assert np.array_equal(m.export(uw.STREAM_RAWBEFORE), pe["brick_rawbefore"])
+        assert np.array_equal(m.export(uw.STREAM_SIDE), pe["side"])
+        assert info["raw_groups"] == pe["n_raw"]
+        assert abs(info["bpw_palette"] - oracle.palette_bits_per_weight(pe)) < 1e-9
+    if formats & uw.FMT_HUFFMAN:
+        assert np.array_equal(m.export(uw.STREAM_LENGTHS), he["lengths"])
+        assert np.array_equal(m.export(uw.STREAM_WORDS), he["words"])
+        assert np.array_equal(m.export(uw.STREAM_OFFSETS), he["offsets"])
+        assert info["stream_bits"] == he["total_bits"]
+        assert abs(info["bpw_huffman"] - oracle.huffman_bits_per_weight(he)) < 1e-9
+    m.free()
+
+
+def test_tiny_config_byte_for_byte():
+    c = synth.CONFIGS["tiny"]
+    _compare(synth.weights(c["rows"], c["cols"], c["seed"], c["p"], c["shift"]))
+
+
+def test_all_patterns_byte_for_byte():
+    _compare(synth.all_bf16_patterns())
+
+
+@pytest.mark.parametrize("seed,rows,cols,p,shift", [(3, 48, 192, 0.01, 12), (4, 16, 64, 0.0, 0),
+                                                     (5, 160, 320, 0.003, 10), (6, 32, 4096, 0.0005, 10)])
+def test_random_shapes_byte_for_byte(seed, rows, cols, p, shift):
+    _compare(synth.weights(rows, cols, seed, p, shift))
+
+
+def test_single_exponent_and_few_exponents():
+    _compare(np.zeros((16, 64), np.uint16))                 # one symbol: phantom code
+    rng = np.random.default_rng(1)
+    e = rng.integers(120, 124, size=(32, 128)).astype(np.uint16)
+    _compare(((e << 7) | rng.integers(0, 256, size=e.shape).astype(np.uint16) & 0x807F).astype(np.uint16))
+
+
+def test_golden_fixture_through_library():
+    w = np.full((16, 64), 120 << 7, dtype=np.uint16)
+    w[0, 1] = 121 << 7
+    w[0, 2] = 122 << 7
+    m = uw.Matrix(w, HOST_ALL)
+    words = m.export(uw.STREAM_WORDS)
+    assert len(words) == 33 and words[0] == 0x58000000 and not words[1:].any()
+    assert list(m.export(uw.STREAM_OFFSETS)) == [0, 258, 514, 770]
+
+
+def test_format_subsets():
+    w = synth.weights(64, 256, 8, 0.004, 12)
+    _compare(w, uw.FMT_HUFFMAN | uw.ENC_HOST_ONLY)
+    _compare(w, uw.FMT_HUFFMAN | uw.FMT_RAWAUX | uw.ENC_HOST_ONLY)
+    _compare(w, uw.FMT_PALETTE | uw.ENC_HOST_ONLY)
+    m = uw.Matrix(w, uw.FMT_HUFFMAN | uw.ENC_HOST_ONLY)
+    with pytest.raises(uw.UwError) as e:
+        m.export(uw.STREAM_NIBBLES)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+
+
+def test_bad_shapes_and_args():
+    for shape in [(15, 64), (16, 96), (0, 64)]:
+        with pytest.raises(uw.UwError) as e:
+            uw.Matrix(np.zeros(shape, np.uint16), HOST_ALL)
+        assert e.value.status == uw.ERR_SHAPE
+    with pytest.raises(uw.UwError) as e:
+        uw.Matrix(np.zeros((16, 64), np.uint16), uw.ENC_HOST_ONLY)
+    assert e.value.status == uw.ERR_INVALID_ARG
+    with pytest.raises(uw.UwError) as e:
+        uw.Matrix(np.zeros((16, 64), np.uint16), 0x8 | uw.ENC_HOST_ONLY)
+    assert e.value.status == uw.ERR_INVALID_ARG
+    h = C.c_void_p()
+    assert uw._lib.uw_encode(None, 16, 64, HOST_ALL, C.byref(h)) == uw.ERR_INVALID_ARG
+    assert "null" in uw.last_error()
+
+
+def test_host_only_handle_rejects_device_calls():
+    m = uw.Matrix(synth.weights(16, 64, 1, 0.0, 0), HOST_ALL)
+    with pytest.raises(uw.UwError) as e:
+        uw._check(uw._lib.uw_matmul(m._h, 8, 8, 1, uw.P4_DIRECT_PALETTE))
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError):
+        uw._check(uw._lib.uw_decode(m._h, 8))
+    with pytest.raises(uw.UwError):
+        m.set_plan([(64, 9, 0)])
+
+
+def test_variant_names():
+    assert uw.variant_name(1, 0) == "small:default"
+    assert uw.variant_name(1024, 0) == "large:default"
+    assert len(uw.variants(1)) > 5 and len(uw.variants(256)) > 5
+    assert uw.variant_name(1, 999) is None
+
+
+def test_bits_per_weight_on_gate_shaped_slice():
+    """North-star size target: >= 20% fewer weight bytes than bf16 in both forms."""
+    w = synth.weights(1024, 4096, 0, 0.0005, 10)
+    inf = uw.Matrix(w, HOST_ALL).info()
+    assert inf["bpw_palette"] < 16 * 0.8 and inf["bpw_huffman"] < 16 * 0.8
