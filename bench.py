@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode + matmul path on one MI355X.
+
+Headline workload: one gate projection, W = 14336 x 4096 bf16 (N(0, 0.02) with
+0.05% of the weights scaled by 2^10), multiplied by one token of bf16
+activations through the direct-palette pipeline: the fused kernel reads the
+sign+mantissa bytes, the 4-bit codes and the raw-group tables and never writes
+the rebuilt weights anywhere (Unweight page, sections 五-七).
+
+A step is one such fused matmul.  Weight copies at distinct addresses are
+rotated so that at least 1 GiB is touched between two uses of the same copy:
+MI355X's 256 MB Infinity Cache would otherwise serve the 90 MB matrix.  Steps
+are captured in a HIP graph and replayed, and timed with events on the stream
+the kernel runs on.
+
+value = effective weight throughput, 2 * rows * cols bytes (the bf16 matrix
+the step multiplies by) per second.  roofline.achieved = the bytes the kernel
+must read and write (compressed streams + activations + outputs) per second,
+against the 8 TB/s HBM peak.  cpu_baseline = the CPU oracle (numpy) doing the
+same decode + matmul on a bounded sample of the rows.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "fused decode+GEMM eff. weight GB/s & TFLOP/s at batch 1–1024; bits/weight"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_small_gate_b1_traffic.json")
+KERNEL_SOURCES = ["decode_gemm_bf16_amd/csrc/fused_small.hip", "decode_gemm_bf16_amd/csrc/recon.h"]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_graph(torch, fn, steps: int, warmup: int, stream, use_graph: bool = True) -> float:
+    """Average ms per call of fn() on `stream`, from HIP events around `steps` calls."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                for _ in range(steps):
+                    fn()
+            with torch.cuda.stream(stream):
+                graph.replay()  # warm replay
+            torch.cuda.synchronize()
+        except Exception as e:  # capture not possible: time eager launches
+            log(f"graph capture unavailable ({e}); timing eager launches")
+            graph = None
+            torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            for _ in range(steps):
+                fn()
+        end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, x, seconds: float) -> dict:
+    """The CPU oracle decoding the palette form and doing the fp64 matmul on
+    2048-row slices of the same matrix, repeated for about `seconds`."""
+    import numpy as np
+    import oracle
+    rows_per = 2048
+    n_slices = w.shape[0] // rows_per
+    encs = [oracle.palette_encode(w[i * rows_per:(i + 1) * rows_per]) for i in range(min(n_slices, 2))]
+    done_rows = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        enc = encs[passes % len(encs)]
+        dec = oracle.palette_decode(enc)
+        y = oracle.matmul_fp64(x, dec)
+        done_rows += dec.shape[0]
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    try:
+        import threadpoolctl
+        threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    eff = 2.0 * done_rows * w.shape[1] / el / 1e9
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(eff, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} passes of oracle palette_decode + fp64 matmul on {rows_per}-row slices of the "
+                      f"same {w.shape[0]}x{w.shape[1]} matrix at batch {x.shape[0]} ({el:.1f} s; numpy decode "
+                      f"single-threaded, BLAS {threads} threads; host {os.cpu_count()} cpus, {cpu_model})"}
+
+
+def load_traffic(algo_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, if they were taken on the current kernel source."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return int(t["hbm_bytes_per_launch"])
+
+
+def sweep(torch, uw, synth, stream, steps, warmup):
+    """All four pipelines and the uncompressed hipBLASLt baseline on the
+    8B-shaped MLP projections at batch 1..1024 (the other configurations)."""
+    import numpy as np
+    c = synth.CONFIGS["mlp_8b"]
+    out = {}
+    xs = synth.activations(1024, 14336, xseed=1)
+    for proj in ("gate", "up", "down"):
+        rows, cols, seed = c[proj]
+        w = synth.weights(rows, cols, seed, c["p"], c["shift"])
+        base = uw.Matrix(w, uw.FMT_HUFFMAN | uw.FMT_PALETTE)
+        base.set_streams(stream)
+        info = base.info()
+        ncopy = max(2, math.ceil((1 << 30) / info["resident_bytes"]))
+        mats = [base] + [base.clone() for _ in range(ncopy - 1)]
+        for m in mats:
+            m.set_streams(stream)
+        wd = uw.bf16_tensor(w)
+        res = {"bpw_palette": info["bpw_palette"], "bpw_huffman": info["bpw_huffman"]}
+        for tokens in (1, 16, 64, 256, 1024):
+            x = uw.bf16_tensor(xs[:tokens, :cols])
+            y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
+            row = {}
+            flops = 2.0 * tokens * rows * cols
+            for p in (1, 2, 3, 4):
+                i = [0]
+
+                def fn(p=p):
+                    mats[i[0] % ncopy].matmul(x, y, tokens, p)
+                    i[0] += 1
+                ms = time_graph(torch, fn, steps=max(20, steps // 10), warmup=warmup, stream=stream,
+                                use_graph=True)
+                row[f"P{p}"] = {"us": round(ms * 1e3, 2), "eff_GBps": round(2.0 * rows * cols / ms / 1e6, 1),
+                                "TFLOPs": round(flops / ms / 1e9, 2)}
+            ms = time_graph(torch, lambda: uw.gemm_bf16(x, wd, y, tokens, rows, cols, stream),
+                            steps=max(20, steps // 10), warmup=warmup, stream=stream)
+            row["bf16_hipblaslt"] = {"us": round(ms * 1e3, 2), "eff_GBps": round(2.0 * rows * cols / ms / 1e6, 1),
+                                     "TFLOPs": round(flops / ms / 1e9, 2)}
+            res[str(tokens)] = row
+            log(proj, tokens, json.dumps(row))
+        out[proj] = res
+        for m in mats:
+            m.free()
+        del wd
+        torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=0, help="weight copies rotated (0: enough for >= 1 GiB)")
+    ap.add_argument("--variant", type=int, default=0, help="fused-kernel variant (0: built-in choice)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this path keeps no state across GPUs and runs no collectives; "
+              f"--gpus {args.gpus} (WORLD_SIZE={world}) is not supported", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_gemm_bf16_amd as uw
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    c = synth.CONFIGS["gate_8b"]
+    rows, cols, tokens = c["rows"], c["cols"], 1
+    log(f"generating {rows}x{cols} weights")
+    w = synth.weights(rows, cols, c["seed"], c["p"], c["shift"])
+    x_bits = synth.activations(tokens, cols, xseed=c["xseed"])
+    t0 = time.perf_counter()
+    base = uw.Matrix(w, uw.FMT_PALETTE | uw.FMT_HUFFMAN)
+    enc_s = time.perf_counter() - t0
+    info = base.info()
+    pal = uw.Matrix(w, uw.FMT_PALETTE)            # direct-palette form only
+    pinfo = pal.info()
+    stream = torch.cuda.Stream()
+    ncopy = args.copies or max(2, math.ceil((1 << 30) / pinfo["resident_bytes"]))
+    mats = [pal] + [pal.clone() for _ in range(ncopy - 1)]
+    for m in mats:
+        m.set_streams(stream)
+        m.set_variant(args.variant)
+    x = uw.bf16_tensor(x_bits)
+    y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
+
+    # algorithmic bytes of one launch: the streams the direct-palette kernel must
+    # read (sign+mantissa, codes, per-brick table, raw side table) + x + y
+    n = rows * cols
+    bricks = n // 1024
+    algo_bytes = n + n // 2 + 8 * bricks + 64 * pinfo["raw_groups"] + 2 * tokens * cols + 4 * tokens * rows
+
+    i = [0]
+
+    def step():
+        mats[i[0] % ncopy].matmul(x, y, tokens, uw.P4_DIRECT_PALETTE)
+        i[0] += 1
+
+    log(f"timing {args.steps} steps over {ncopy} copies ({ncopy * pinfo['resident_bytes'] / 2**30:.2f} GiB)")
+    ms = time_graph(torch, step, args.steps, args.warmup, stream, use_graph=not args.no_graph)
+    t_s = ms / 1e3
+    value = 2.0 * n / t_s / 1e9
+    achieved = algo_bytes / t_s / 1e9
+
+    # reference points: measured copy ceiling and the uncompressed library GEMV
+    cbytes = 1 << 30
+    src = torch.empty(cbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(cbytes, dtype=torch.uint8, device="cuda")
+    cms = time_graph(torch, lambda: uw.device_copy(src, dst, cbytes, stream), 20, 3, stream)
+    copy_gbps = 2.0 * cbytes / (cms / 1e3) / 1e9
+    del src, dst
+    wd_copies = max(2, math.ceil((1 << 30) / (2 * n)))
+    wds = [uw.bf16_tensor(w) for _ in range(wd_copies)]
+    j = [0]
+
+    def base_step():
+        uw.gemm_bf16(x, wds[j[0] % wd_copies], y, tokens, rows, cols, stream)
+        j[0] += 1
+    bms = time_graph(torch, base_step, max(100, args.steps // 5), 10, stream)
+    del wds
+    torch.cuda.empty_cache()
+
+    traffic = load_traffic(algo_bytes)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights with 0.05% x2^10 outliers; N(0,1) bf16 activations)",
+        "config": {
+            "workload": "gate_proj 14336x4096 bf16, direct-palette fused decode+GEMV, batch 1 token",
+            "rows": rows, "cols": cols, "tokens": tokens, "pipeline": "P4 direct palette",
+            "bits_per_weight": round(pinfo["bpw_palette"], 4),
+            "weight_byte_reduction": round(1 - pinfo["bpw_palette"] / 16, 4),
+            "copies_rotated": ncopy, "variant": uw.variant_name(tokens, args.variant),
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(algo_bytes), "avg_launch_us": round(ms * 1e3, 3),
+            "kernel": "fused_small_kernel<8,1,false,2>", "kernel_sha": kernel_sha(),
+        },
+        "extra": {
+            "tflops": round(2.0 * n * tokens / t_s / 1e12, 4),
+            "bits_per_weight_huffman": round(info["bpw_huffman"], 4),
+            "raw_group_fraction": round(pinfo["raw_groups"] / pinfo["groups"], 5),
+            "encode_s_host": round(enc_s, 2),
+            "measured_copy_GBps": round(copy_gbps, 1),
+            "frac_of_measured_copy": round(achieved / copy_gbps, 4),
+            "uncompressed_hipblaslt_us": round(bms * 1e3, 3),
+            "uncompressed_hipblaslt_eff_GBps": round(2.0 * n / (bms / 1e3) / 1e9, 1),
+            "speedup_vs_uncompressed": round(bms / ms, 3),
+            "roofline_effective_GBps": round(HBM_PEAK_GBPS * 16 / pinfo["bpw_palette"], 1),
+        },
+    }
+    if args.sweep:
+        result["sweep"] = sweep(torch, uw, synth, stream, args.steps, args.warmup)
+    if not args.no_cpu:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, x_bits, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    for m in mats:
+        m.free()
+    base.free()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
