@@ -28,7 +28,7 @@ EXPORTED = [
     "uw_encode", "uw_decode", "uw_matmul", "uw_preprocess", "uw_set_streams", "uw_set_scratch", "uw_set_plan",
     "uw_set_variant", "uw_variant_name", "uw_query", "uw_export", "uw_clone", "uw_free", "uw_last_error", "uw_silu_mul",
     "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_stack_forward", "uw_stack_workspace_bytes",
-    "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy",
+    "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy", "uw_device_read",
 ]
 
 
@@ -95,6 +95,7 @@ def _load() -> C.CDLL:
         "uw_device_cu_count": ([], i32),
         "uw_gemm_bf16": ([vp, vp, vp, i64, i64, i64, vp], st),
         "uw_device_copy": ([vp, vp, C.c_size_t, vp], st),
+        "uw_device_read": ([vp, vp, C.c_size_t, vp], st),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -241,6 +242,11 @@ def gemm_bf16(x, w, y, tokens: int, rows: int, cols: int, stream=None) -> None:
 
 def device_copy(src, dst, nbytes: int, stream=None) -> None:
     _check(_lib.uw_device_copy(_ptr(src), _ptr(dst), nbytes, _stream_ptr(stream)))
+
+
+def device_read(src, sink, nbytes: int, stream=None) -> None:
+    """Read nbytes of src (HBM read ceiling); sink: >= 16 bytes of device memory."""
+    _check(_lib.uw_device_read(_ptr(src), _ptr(sink), nbytes, _stream_ptr(stream)))
 
 
 def mlp_workspace_bytes(tokens: int, inter: int) -> int:

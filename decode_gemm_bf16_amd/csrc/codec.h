@@ -18,7 +18,7 @@ constexpr int kRun = 16;                                // weights of one row pe
 constexpr int kChunk = 256;                             // Huffman symbols per chunk
 constexpr int kLmax = 12;                               // longest code, bits
 constexpr int kLutSize = 1 << kLmax;                    // decode table entries
-constexpr int kStreamPadWords = 4;                      // zero words after the stream
+constexpr int kStreamPadWords = 8;                      // zero words after the stream
 
 struct HostFormat {
   int64_t rows = 0, cols = 0;

@@ -11,16 +11,29 @@
 // the same matrix-core time, which is negligible next to the HBM stream.
 //
 // Work split: one workgroup per 16-row brick-row (x `ksplit` slices of K);
-// its waves take every WAVES-th brick along K, so a workgroup sweeps a
-// contiguous stretch of the stream.  Partial sums meet in LDS; with ksplit > 1
-// the slices add into a zeroed Y with float atomics.
+// its waves take every WAVES-th group of U bricks along K.  Loads are software
+// pipelined: while stage i (U bricks) is rebuilt and multiplied, every load of
+// stage i+1 is in flight -- weights, activations and, for bricks holding raw
+// groups, the raw side-table bytes, whose addresses come from the per-brick
+// table read one stage earlier still.  Partial sums meet in LDS; with
+// ksplit > 1 the slices add into a zeroed Y with float atomics.
 #include "kernels.h"
 #include "recon.h"
 
 namespace uw {
 namespace {
 
-template <int WAVES, int TB, bool EXPM, int UNROLL>
+template <int U, int TB, bool EXPM>
+struct Stage {
+  u32x4 s[U];          // sign+mantissa bytes
+  u32x4 e[U];          // exponent bytes (exponent mode) or raw side-table bytes
+  u32x2 n[U];          // 4-bit codes (palette mode)
+  u32x4 x[U][TB][2];   // activations: B operand of the two k-halves
+  uint32_t anyraw[U];  // wave-uniform: some row of the brick is raw
+  bool raw[U];         // this lane's row is raw
+};
+
+template <int WAVES, int TB, bool EXPM, int U>
 __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint32_t lut0, uint32_t lut1, uint32_t lut2, uint32_t lut3,
@@ -34,64 +47,99 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   const int hi = (int)(((int64_t)(blockIdx.y + 1) * kbn) / ksplit);
   const size_t brick_row0 = (size_t)blockIdx.x * kbn;
   const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
+  constexpr int STEP = WAVES * U;
 
   f32x4 acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kb0 = lo + wave; kb0 < hi; kb0 += WAVES * UNROLL) {
-    u32x4 s[UNROLL];
-    u32x4 e[UNROLL];
-    u32x2 n[UNROLL];
-    uint2 m[UNROLL];
+  // per-brick table of the stage that will be fetched next
+  uint2 mnext[U];
+  auto load_meta = [&](int kb0) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int kb = kb0 + u * WAVES;
-      if (kb < hi) {
-        const size_t b = brick_row0 + kb;
-        s[u] = *(const u32x4*)(sm + b * 1024 + lane * 16);
-        if (EXPM) {
-          e[u] = *(const u32x4*)(codes + b * 1024 + lane * 16);
-        } else {
-          n[u] = *(const u32x2*)(codes + b * 512 + lane * 8);
-          m[u] = meta[b];
-        }
-      }
+      mnext[u] = (!EXPM && kb < hi) ? meta[brick_row0 + kb] : uint2{0u, 0u};
     }
+  };
+  auto fetch = [&](Stage<U, TB, EXPM>& st, int kb0) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int kb = kb0 + u * WAVES;
       if (kb >= hi) break;
-      uint32_t p[8];
+      const size_t b = brick_row0 + kb;
+      st.s[u] = *(const u32x4*)(sm + b * 1024 + lane * 16);
       if (EXPM) {
-        rebuild_exp(s[u], e[u], p);
+        st.e[u] = *(const u32x4*)(codes + b * 1024 + lane * 16);
       } else {
-        rebuild_palette(s[u], n[u], lut, p);
-        const uint32_t map = m[u].x;
-        if (map) {                     // some row of this brick is stored raw
-          if ((map >> r) & 1u) {
-            const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-            const u32x4 ev = *(const u32x4*)(side + ((size_t)m[u].y + rank) * 64 + q * 16);
-            rebuild_exp(s[u], ev, p);
-          }
+        st.n[u] = *(const u32x2*)(codes + b * 512 + lane * 8);
+        const uint32_t map = mnext[u].x;
+        st.anyraw[u] = map;
+        st.raw[u] = (map >> r) & 1u;
+        if (map && st.raw[u]) {
+          const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
+          st.e[u] = *(const u32x4*)(side + ((size_t)mnext[u].y + rank) * 64 + q * 16);
         }
       }
-      const bf16x8 a0 = as_bf16x8(p[0], p[1], p[2], p[3]);
-      const bf16x8 a1 = as_bf16x8(p[4], p[5], p[6], p[7]);
       const int kx = kb * 64 + q * 16;
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
         const int tok = t * 16 + r;
-        u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
+        st.x[u][t][0] = u32x4{0u, 0u, 0u, 0u};
+        st.x[u][t][1] = u32x4{0u, 0u, 0u, 0u};
         if (tok < tokens) {
           const uint16_t* xp = x + (size_t)tok * cols + kx;
-          x0 = *(const u32x4*)xp;
-          x1 = *(const u32x4*)(xp + 8);
+          st.x[u][t][0] = *(const u32x4*)xp;
+          st.x[u][t][1] = *(const u32x4*)(xp + 8);
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x0), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x1), acc[t], 0, 0, 0);
       }
     }
+  };
+  auto compute = [&](const Stage<U, TB, EXPM>& st, int kb0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kb0 + u * WAVES >= hi) break;
+      uint32_t p[8];
+      if (EXPM) {
+        rebuild_exp(st.s[u], st.e[u], p);
+      } else {
+        uint32_t v[4];
+        palette_v(st.n[u], lut, v);
+        if (st.anyraw[u]) {  // wave-uniform: the brick holds a raw group
+          if (st.raw[u]) {
+            v[0] = rot_exp(st.e[u].x);
+            v[1] = rot_exp(st.e[u].y);
+            v[2] = rot_exp(st.e[u].z);
+            v[3] = rot_exp(st.e[u].w);
+          }
+        }
+        rebuild_v(st.s[u], v, p);
+      }
+      const bf16x8 a0 = as_bf16x8(p[0], p[1], p[2], p[3]);
+      const bf16x8 a1 = as_bf16x8(p[4], p[5], p[6], p[7]);
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(st.x[u][t][0]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[u][t][1]), acc[t], 0, 0, 0);
+      }
+    }
+  };
+
+  Stage<U, TB, EXPM> sa, sb;
+  int kb = lo + wave;
+  load_meta(kb);
+  fetch(sa, kb);
+  load_meta(kb + STEP);
+  while (kb < hi) {
+    if (kb + STEP < hi) fetch(sb, kb + STEP);
+    load_meta(kb + 2 * STEP);
+    compute(sa, kb);
+    kb += STEP;
+    if (kb >= hi) break;
+    if (kb + STEP < hi) fetch(sa, kb + STEP);
+    load_meta(kb + 2 * STEP);
+    compute(sb, kb);
+    kb += STEP;
   }
 
   // D layout of the 16x16 result: lane l holds rows 4*(l/16)+0..3, column l%16.
@@ -118,28 +166,28 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   }
 }
 
-template <int WAVES, int TB, bool EXPM, int UNROLL>
+template <int WAVES, int TB, bool EXPM, int U>
 hipError_t launch_one(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
   dim3 grid((unsigned)(w.rows / 16), (unsigned)ksplit);
-  hipLaunchKernelGGL((fused_small_kernel<WAVES, TB, EXPM, UNROLL>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
+  hipLaunchKernelGGL((fused_small_kernel<WAVES, TB, EXPM, U>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                      w.meta, w.side, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens, (int)w.rows,
                      (int)w.cols, ksplit);
   return hipGetLastError();
 }
 
-template <int WAVES, int TB, int UNROLL>
+template <int WAVES, int TB, int U>
 hipError_t launch_mode(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
-  return w.exp_mode ? launch_one<WAVES, TB, true, UNROLL>(w, x, y, tokens, ksplit, s)
-                    : launch_one<WAVES, TB, false, UNROLL>(w, x, y, tokens, ksplit, s);
+  return w.exp_mode ? launch_one<WAVES, TB, true, U>(w, x, y, tokens, ksplit, s)
+                    : launch_one<WAVES, TB, false, U>(w, x, y, tokens, ksplit, s);
 }
 
-template <int WAVES, int UNROLL>
+template <int WAVES, int U>
 hipError_t launch_tb(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
   switch ((tokens + 15) / 16) {
-    case 1: return launch_mode<WAVES, 1, UNROLL>(w, x, y, tokens, ksplit, s);
-    case 2: return launch_mode<WAVES, 2, UNROLL>(w, x, y, tokens, ksplit, s);
-    case 3: return launch_mode<WAVES, 3, UNROLL>(w, x, y, tokens, ksplit, s);
-    default: return launch_mode<WAVES, 4, UNROLL>(w, x, y, tokens, ksplit, s);
+    case 1: return launch_mode<WAVES, 1, U>(w, x, y, tokens, ksplit, s);
+    case 2: return launch_mode<WAVES, 2, U>(w, x, y, tokens, ksplit, s);
+    case 3: return launch_mode<WAVES, 3, U>(w, x, y, tokens, ksplit, s);
+    default: return launch_mode<WAVES, 4, U>(w, x, y, tokens, ksplit, s);
   }
 }
 

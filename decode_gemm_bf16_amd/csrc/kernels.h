@@ -46,6 +46,7 @@ struct HuffDev {
   const uint8_t* sm;        // EMIT_BF16
   const uint2* meta;        // EMIT_NIBBLE: per-brick raw map
   const uint8_t* code_of;   // EMIT_NIBBLE: 256 entries, code of each palette exponent
+  uint64_t total_bits;      // payload bits of the stream (words holds 8 zero words more)
   int64_t rows, cols;
 };
 hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipStream_t s);
@@ -57,5 +58,6 @@ hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t 
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_read(const void* src, void* sink, size_t bytes, hipStream_t s);
 
 }  // namespace uw

@@ -42,9 +42,34 @@ __global__ void zero_kernel(float* __restrict__ p, int64_t n) {
   }
 }
 
-__global__ void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+// Each thread keeps four independent 16-byte loads in flight.
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  if (base + 768 < n16) {
+    const u32x4 a = src[base], b = src[base + 256], c = src[base + 512], d = src[base + 768];
+    dst[base] = a;
+    dst[base + 256] = b;
+    dst[base + 512] = c;
+    dst[base + 768] = d;
+  } else {
+    for (int64_t i = base; i < n16 && i < base + 1024; i += 256) dst[i] = src[i];
+  }
+}
+
+// Read-only stream: four 16-byte loads in flight per thread, XOR-folded so
+// the loads cannot be dropped; lanes whose fold is nonzero write it to sink
+// (any of them: the value only keeps the loads alive).
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ sink,
+                                                   int64_t n16) {
+  const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if (base + 768 < n16) {
+    acc = src[base] ^ src[base + 256] ^ src[base + 512] ^ src[base + 768];
+  } else {
+    for (int64_t i = base; i < n16 && i < base + 1024; i += 256) acc ^= src[i];
+  }
+  if ((acc.x | acc.y | acc.z | acc.w) == 0x9E3779B9u) *sink = acc;
 }
 
 // Palette form -> row-major bf16, one wave per brick (lane = run).
@@ -100,8 +125,16 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t s) {
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const int64_t n16 = (int64_t)(bytes / 16);
   if (n16 <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 256 * 16);
+  const int64_t blocks = (n16 + 1023) / 1024;
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)dst, n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_read(const void* src, void* sink, size_t bytes, hipStream_t s) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = (n16 + 1023) / 1024;
+  hipLaunchKernelGGL(read_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4*)src, (u32x4*)sink, n16);
   return hipGetLastError();
 }
 

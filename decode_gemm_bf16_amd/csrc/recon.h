@@ -44,6 +44,11 @@ __device__ __forceinline__ void assemble_e(uint32_t S, uint32_t E, uint32_t& p01
   p23 = perm(H, L, 0x07030602u);
 }
 
+// Four exponent bytes rotated right by one bit each.
+__device__ __forceinline__ uint32_t rot_exp(uint32_t E) {
+  return ((E >> 1) & 0x7F7F7F7Fu) | ((E << 7) & 0x80808080u);
+}
+
 // 16-entry palette lookup of 8 codes packed in N (byte b: code b low nibble,
 // code b+4 high nibble).  lut[q] holds entries 4q..4q+3.  Low three code bits
 // index two 8-entry halves with one byte permute each; the fourth bit then
@@ -57,16 +62,25 @@ __device__ __forceinline__ void palette_lookup(uint32_t N, const uint32_t lut[4]
   Vb = perm(perm(lut[3], lut[2], ib), perm(lut[1], lut[0], ib), sb);
 }
 
+// Rotated exponents of one lane's 16 weights from its 8 code bytes.
+__device__ __forceinline__ void palette_v(const u32x2& n, const uint32_t lut[4], uint32_t v[4]) {
+  palette_lookup(n.x, lut, v[0], v[1]);
+  palette_lookup(n.y, lut, v[2], v[3]);
+}
+
+__device__ __forceinline__ void rebuild_v(const u32x4& s, const uint32_t v[4], uint32_t p[8]) {
+  assemble_v(s.x, v[0], p[0], p[1]);
+  assemble_v(s.y, v[1], p[2], p[3]);
+  assemble_v(s.z, v[2], p[4], p[5]);
+  assemble_v(s.w, v[3], p[6], p[7]);
+}
+
 // One lane's 16 weights of a brick -> 8 dwords of bf16 pairs, weights in order.
 __device__ __forceinline__ void rebuild_palette(const u32x4& s, const u32x2& n, const uint32_t lut[4],
                                                 uint32_t p[8]) {
-  uint32_t v0, v1, v2, v3;
-  palette_lookup(n.x, lut, v0, v1);
-  palette_lookup(n.y, lut, v2, v3);
-  assemble_v(s.x, v0, p[0], p[1]);
-  assemble_v(s.y, v1, p[2], p[3]);
-  assemble_v(s.z, v2, p[4], p[5]);
-  assemble_v(s.w, v3, p[6], p[7]);
+  uint32_t v[4];
+  palette_v(n, lut, v);
+  rebuild_v(s, v, p);
 }
 
 __device__ __forceinline__ void rebuild_exp(const u32x4& s, const u32x4& e, uint32_t p[8]) {

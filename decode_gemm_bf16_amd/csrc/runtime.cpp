@@ -191,6 +191,7 @@ uw::HuffDev huff_view(const uw_matrix* h) {
   d.sm = h->d_sm;
   d.meta = h->d_meta;
   d.code_of = h->d_code_of;
+  d.total_bits = h->hf.stream_bits;
   d.rows = h->rows;
   d.cols = h->cols;
   return d;
@@ -810,6 +811,13 @@ uw_status uw_device_copy(const void* src, void* dst, size_t bytes, void* stream)
   if (!src || !dst) return fail(UW_ERR_INVALID_ARG, "null pointer");
   if (bytes % 16) return fail(UW_ERR_INVALID_ARG, "size must be a multiple of 16");
   UW_HIP(uw::launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+  return UW_OK;
+}
+
+uw_status uw_device_read(const void* src, void* sink, size_t bytes, void* stream) {
+  if (!src || !sink) return fail(UW_ERR_INVALID_ARG, "null pointer");
+  if (bytes % 16) return fail(UW_ERR_INVALID_ARG, "size must be a multiple of 16");
+  UW_HIP(uw::launch_read(src, sink, bytes, static_cast<hipStream_t>(stream)));
   return UW_OK;
 }
 

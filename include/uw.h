@@ -105,7 +105,7 @@ typedef struct {
   uint8_t code_lengths[256];
   uint64_t raw_groups, groups;
   uint64_t stream_bits;        /* Huffman payload bits (without padding)        */
-  uint64_t stream_words;       /* payload words (without the 4 padding words)   */
+  uint64_t stream_words;       /* payload words (without the 8 padding words)   */
   double bpw_palette;          /* bits/weight of the direct-palette form        */
   double bpw_huffman;          /* bits/weight of the Huffman form               */
   double bpw_resident;         /* bits/weight of what this handle stores        */
@@ -227,6 +227,11 @@ uw_status uw_gemm_bf16(const uint16_t* x_dev, const uint16_t* w_dev, float* y_de
 /* Plain device copy of `bytes` bytes (multiple of 16) with 16-byte loads and
  * stores: the measured HBM ceiling. */
 uw_status uw_device_copy(const void* src_dev, void* dst_dev, size_t bytes, void* stream);
+
+/* Read `bytes` bytes (multiple of 16) with 16-byte loads and XOR them into
+ * 16 bytes at sink_dev: the measured HBM read ceiling (a fused matmul only
+ * reads weights). */
+uw_status uw_device_read(const void* src_dev, void* sink_dev, size_t bytes, void* stream);
 
 #ifdef __cplusplus
 }
