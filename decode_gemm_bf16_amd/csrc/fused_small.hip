@@ -36,8 +36,9 @@ struct Stage {
 template <int WAVES, int TB, bool EXPM, int U>
 __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
-    const uint8_t* __restrict__ side, uint32_t lut0, uint32_t lut1, uint32_t lut2, uint32_t lut3,
-    const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols, int ksplit) {
+    const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
+    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
+    int ksplit) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;  // row inside the brick (A operand row) / token inside a block (B column)
@@ -46,12 +47,27 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   const int lo = (int)(((int64_t)blockIdx.y * kbn) / ksplit);
   const int hi = (int)(((int64_t)(blockIdx.y + 1) * kbn) / ksplit);
   const size_t brick_row0 = (size_t)blockIdx.x * kbn;
-  const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
+  const uint32_t lut[4] = {in_vgpr(lut0), in_vgpr(lut1), in_vgpr(lut2), in_vgpr(lut3)};
   constexpr int STEP = WAVES * U;
-
-  f32x4 acc[TB];
+  const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
+  const rsrc_t rs_sm = make_rsrc(sm, nweights);
+  const rsrc_t rs_codes = make_rsrc(codes, EXPM ? nweights : nweights / 2);
+  const rsrc_t rs_side = make_rsrc(side, side_bytes);
+  const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
+  // per-lane byte offsets, fixed for the whole kernel
+  const uint32_t lane16 = lane * 16, lane8 = lane * 8;
+  uint32_t xlane[TB];
+  bool xlive[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TB; ++t) {
+    const int tok = t * 16 + r;
+    xlive[t] = tok < tokens;
+    xlane[t] = ((uint32_t)tok * cols + q * 16) * 2;
+  }
+
+  f32x4 acc[TB], acc2[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) acc[t] = acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // per-brick table of the stage that will be fetched next
   uint2 mnext[U];
@@ -67,30 +83,27 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
     for (int u = 0; u < U; ++u) {
       const int kb = kb0 + u * WAVES;
       if (kb >= hi) break;
-      const size_t b = brick_row0 + kb;
-      st.s[u] = *(const u32x4*)(sm + b * 1024 + lane * 16);
+      const uint32_t b = (uint32_t)brick_row0 + kb;
+      st.s[u] = ld16(rs_sm, lane16, b * 1024);
       if (EXPM) {
-        st.e[u] = *(const u32x4*)(codes + b * 1024 + lane * 16);
+        st.e[u] = ld16(rs_codes, lane16, b * 1024);
       } else {
-        st.n[u] = *(const u32x2*)(codes + b * 512 + lane * 8);
+        st.n[u] = ld8(rs_codes, lane8, b * 512);
         const uint32_t map = mnext[u].x;
         st.anyraw[u] = map;
         st.raw[u] = (map >> r) & 1u;
         if (map && st.raw[u]) {
           const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-          st.e[u] = *(const u32x4*)(side + ((size_t)mnext[u].y + rank) * 64 + q * 16);
+          st.e[u] = ld16(rs_side, (mnext[u].y + rank) * 64 + q * 16, 0);
         }
       }
-      const int kx = kb * 64 + q * 16;
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
-        const int tok = t * 16 + r;
         st.x[u][t][0] = u32x4{0u, 0u, 0u, 0u};
         st.x[u][t][1] = u32x4{0u, 0u, 0u, 0u};
-        if (tok < tokens) {
-          const uint16_t* xp = x + (size_t)tok * cols + kx;
-          st.x[u][t][0] = *(const u32x4*)xp;
-          st.x[u][t][1] = *(const u32x4*)(xp + 8);
+        if (xlive[t]) {
+          st.x[u][t][0] = ld16(rs_x, xlane[t], kb * 128);
+          st.x[u][t][1] = ld16(rs_x, xlane[t] + 16, kb * 128);
         }
       }
     }
@@ -99,9 +112,9 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (kb0 + u * WAVES >= hi) break;
-      uint32_t p[8];
+      u32x4 w0, w1;
       if (EXPM) {
-        rebuild_exp(st.s[u], st.e[u], p);
+        rebuild_exp2(st.s[u], st.e[u], w0, w1);
       } else {
         uint32_t v[4];
         palette_v(st.n[u], lut, v);
@@ -113,15 +126,17 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
             v[3] = rot_exp(st.e[u].w);
           }
         }
-        rebuild_v(st.s[u], v, p);
+        rebuild_v2(st.s[u], v, w0, w1);
       }
-      const bf16x8 a0 = as_bf16x8(p[0], p[1], p[2], p[3]);
-      const bf16x8 a1 = as_bf16x8(p[4], p[5], p[6], p[7]);
+      const bf16x8 a0 = as_bf16x8(w0);
+      const bf16x8 a1 = as_bf16x8(w1);
+      // the two k-halves go to separate accumulators (no back-to-back dependency)
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
+      for (int t = 0; t < TB; ++t)
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(st.x[u][t][0]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[u][t][1]), acc[t], 0, 0, 0);
-      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+        acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[u][t][1]), acc2[t], 0, 0, 0);
     }
   };
 
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   // D layout of the 16x16 result: lane l holds rows 4*(l/16)+0..3, column l%16.
   __shared__ f32x4 red[WAVES][TB][64];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
+  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t] + acc2[t];
   __syncthreads();
   for (int i = threadIdx.x; i < TB * 64; i += WAVES * 64) {
     const int t = i >> 6, l = i & 63;
@@ -170,8 +185,8 @@ template <int WAVES, int TB, bool EXPM, int U>
 hipError_t launch_one(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
   dim3 grid((unsigned)(w.rows / 16), (unsigned)ksplit);
   hipLaunchKernelGGL((fused_small_kernel<WAVES, TB, EXPM, U>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
-                     w.meta, w.side, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens, (int)w.rows,
-                     (int)w.cols, ksplit);
+                     w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
+                     (int)w.rows, (int)w.cols, ksplit);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ struct FusedW {
   const uint8_t* codes;    // palette mode: 4-bit codes (0.5 B/weight); exponent mode: exponent bytes
   const uint2* meta;       // palette mode: per brick {raw map, raw groups before}
   const uint8_t* side;     // palette mode: raw groups' exponent bytes
+  uint64_t side_bytes;     // size of side (at least 64)
   uint32_t lut[4];         // palette mode: entry i = rotr8(palette[i], 1) at byte i%4 of lut[i/4]
   int64_t rows, cols;
   bool exp_mode;           // codes are exponent bytes (pipeline 2)

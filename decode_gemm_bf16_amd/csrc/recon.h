@@ -83,6 +83,36 @@ __device__ __forceinline__ void rebuild_palette(const u32x4& s, const u32x2& n, 
   rebuild_v(s, v, p);
 }
 
+// Same, straight into the two MFMA operand vectors (weights 0-7 and 8-15).
+__device__ __forceinline__ void rebuild_v2(const u32x4& s, const uint32_t v[4], u32x4& a0, u32x4& a1) {
+  uint32_t p[8];
+  assemble_v(s.x, v[0], p[0], p[1]);
+  assemble_v(s.y, v[1], p[2], p[3]);
+  assemble_v(s.z, v[2], p[4], p[5]);
+  assemble_v(s.w, v[3], p[6], p[7]);
+  a0 = u32x4{p[0], p[1], p[2], p[3]};
+  a1 = u32x4{p[4], p[5], p[6], p[7]};
+}
+
+__device__ __forceinline__ void rebuild_exp2(const u32x4& s, const u32x4& e, u32x4& a0, u32x4& a1) {
+  uint32_t p[8];
+  assemble_e(s.x, e.x, p[0], p[1]);
+  assemble_e(s.y, e.y, p[2], p[3]);
+  assemble_e(s.z, e.z, p[4], p[5]);
+  assemble_e(s.w, e.w, p[6], p[7]);
+  a0 = u32x4{p[0], p[1], p[2], p[3]};
+  a1 = u32x4{p[4], p[5], p[6], p[7]};
+}
+
+// A wave-uniform value copied into a vector register once, so that loops do not
+// re-materialise it from a scalar register at every use (v_perm_b32 takes at
+// most one scalar operand).
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t s) {
+  uint32_t v;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+  return v;
+}
+
 __device__ __forceinline__ void rebuild_exp(const u32x4& s, const u32x4& e, uint32_t p[8]) {
   assemble_e(s.x, e.x, p[0], p[1]);
   assemble_e(s.y, e.y, p[2], p[3]);
@@ -96,5 +126,23 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, 
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Raw buffer access: a scalar resource (base, size) plus a per-lane 32-bit byte
+// offset and a wave-uniform byte offset.  Loads cost no per-lane address
+// arithmetic, and the per-lane part of an offset is computed once per kernel.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ u32x2 ld8(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
 
 }  // namespace uw

@@ -176,6 +176,7 @@ uw::FusedW fused_view(const uw_matrix* h, bool exp_mode, const uint8_t* codes) {
   f.codes = codes;
   f.meta = h->d_meta;
   f.side = h->d_side;
+  f.side_bytes = std::max<uint64_t>(h->hf.n_raw * 64, 64);
   for (int i = 0; i < 4; ++i) f.lut[i] = h->lut_v[i];
   f.rows = h->rows;
   f.cols = h->cols;
@@ -404,6 +405,8 @@ uw_status uw_encode(const uint16_t* w_host, int64_t rows, int64_t cols, uint32_t
   if (rows <= 0 || cols <= 0 || rows % 16 || cols % 64)
     return fail(UW_ERR_SHAPE, "shape %lldx%lld: rows must be a multiple of 16 and cols of 64", (long long)rows,
                 (long long)cols);
+  if (rows * cols >= (int64_t(1) << 31))
+    return fail(UW_ERR_SHAPE, "matrix of %lld weights: at most 2^31 - 1 weights per matrix", (long long)(rows * cols));
   uw_matrix* h = new (std::nothrow) uw_matrix;
   if (!h) return fail(UW_ERR_OOM, "host allocation failed");
   h->rows = rows;

@@ -32,7 +32,8 @@ const Named kSmall[] = {
 // large batch: kind 1, {tile, ksplit}
 const Named kLarge[] = {
     {{1, 0, 1, 0, 0}, "large:t0(4x64r x128t):k1"}, {{1, 0, 2, 0, 0}, "large:t0(4x64r x128t):k2"},
-    {{1, 0, 4, 0, 0}, "large:t0(4x64r x128t):k4"}, {{1, 0, 1, 0, 1}, "large:t1(4x32r x128t):k1"},
+    {{1, 0, 4, 0, 0}, "large:t0(4x64r x128t):k4"}, {{1, 0, 8, 0, 0}, "large:t0(4x64r x128t):k8"},
+    {{1, 0, 16, 0, 0}, "large:t0(4x64r x128t):k16"}, {{1, 0, 1, 0, 1}, "large:t1(4x32r x128t):k1"},
     {{1, 0, 2, 0, 1}, "large:t1(4x32r x128t):k2"}, {{1, 0, 1, 0, 2}, "large:t2(2x64r x128t):k1"},
     {{1, 0, 2, 0, 2}, "large:t2(2x64r x128t):k2"}, {{1, 0, 1, 0, 3}, "large:t3(4x64r x64t):k1"},
     {{1, 0, 2, 0, 3}, "large:t3(4x64r x64t):k2"},
@@ -56,16 +57,26 @@ const char* variant_name(int64_t tokens, int id) {
   return tokens <= 64 ? kSmall[id - 1].name : kLarge[id - 1].name;
 }
 
+// Built-in choice when no plan is set (measured on MI355X with the 8B-shaped
+// projections; the autotuner refines it per matrix and batch).
 Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   const int64_t brows = rows / 16, kbn = cols / 64;
   if (tokens <= 64) {
-    Variant v{0, 8, 1, 2, 0};
-    if (brows < 512) v.ksplit = (int)std::min<int64_t>({4, (1024 + brows - 1) / brows, kbn});
+    // one 16-row brick-row per workgroup already gives >= 4096 waves for the
+    // 4096-row down projection; K is split only for very short matrices
+    Variant v{0, tokens <= 16 ? 16 : 8, 1, 1, 0};
+    if (brows < 128) v.ksplit = (int)std::min<int64_t>({8, (256 + brows - 1) / brows, kbn});
     return v;
   }
-  Variant v{1, 0, 1, 0, 0};
-  const int64_t wgs = ((brows + 15) / 16) * ((tokens + 127) / 128);
-  if (wgs < 512) v.ksplit = (int)std::min<int64_t>({4, (512 + wgs - 1) / wgs, kbn});
+  const int64_t tblk = (tokens + 127) / 128;
+  const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
+  const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tile 1: 128 rows per workgroup
+  Variant v{1, 0, 1, 0, wg0 >= 384 ? 0 : 1};
+  const int64_t wgs = v.tile == 0 ? wg0 : wg1;
+  if (wgs < 128)
+    v.ksplit = (int)std::min<int64_t>({8, (256 + wgs - 1) / wgs, kbn});
+  else if (wgs < 384 && kbn >= 128)
+    v.ksplit = 2;
   return v;
 }
 
