@@ -41,6 +41,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_small_gate_b1_traffic.txt")
 KERNEL_SOURCES = ["decode_gemm_bf16_amd/csrc/fused_small.hip", "decode_gemm_bf16_amd/csrc/recon.h"]
 
 
+def time_graph(torch, fn, steps, warmup, stream, use_graph=True):
+    from decode_gemm_bf16_amd.tune import time_graph as tg
+    return tg(torch, fn, steps, warmup, stream, use_graph)
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -50,40 +55,6 @@ def kernel_sha() -> str:
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def time_graph(torch, fn, steps: int, warmup: int, stream, use_graph: bool = True) -> float:
-    """Average ms per call of fn() on `stream`, from HIP events around `steps` calls."""
-    with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            fn()
-    torch.cuda.synchronize()
-    graph = None
-    if use_graph:
-        try:
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph, stream=stream):
-                for _ in range(steps):
-                    fn()
-            with torch.cuda.stream(stream):
-                graph.replay()  # warm replay
-            torch.cuda.synchronize()
-        except Exception as e:  # capture not possible: time eager launches
-            log(f"graph capture unavailable ({e}); timing eager launches")
-            graph = None
-            torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            for _ in range(steps):
-                fn()
-        end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
 
 
 def cpu_baseline(w, x, seconds: float) -> dict:
@@ -162,6 +133,8 @@ def sweep(torch, uw, synth, stream, steps, warmup):
         mats = [base] + [base.clone() for _ in range(ncopy - 1)]
         for m in mats:
             m.set_streams(stream)
+        from decode_gemm_bf16_amd.tune import share_scratch
+        shared = share_scratch(torch, mats)  # noqa: F841 (kept alive while timing)
         nwd = max(2, math.ceil((1 << 30) / (2 * rows * cols)))
         wds = [uw.bf16_tensor(w) for _ in range(nwd)]
         res = {"bpw_palette": info["bpw_palette"], "bpw_huffman": info["bpw_huffman"]}
@@ -198,6 +171,80 @@ def sweep(torch, uw, synth, stream, steps, warmup):
     return out
 
 
+def stack_bench(torch, uw, synth, tokens_list, steps: int):
+    """The 70B-shaped stack: 80 SwiGLU layers (gate/up 28672x8192, down
+    8192x28672), even layers hard (Huffman, runtime palette transcode), odd
+    layers easy (direct palette).  Four distinct layers are generated and
+    encoded; the 80 layers are device copies of them at distinct addresses
+    (generation time), so every pass streams ~80 GB of distinct memory."""
+    import numpy as np
+    from decode_gemm_bf16_amd.tune import tune_split
+    c = synth.CONFIGS["stack_70b"]
+    L = c["layers"]
+    hidden, inter = c["gate"][1], c["gate"][0]
+    distinct = []
+    t0 = time.perf_counter()
+    for l in range(4):
+        hard = l % 2 == 0
+        fmt = (uw.FMT_HUFFMAN | uw.FMT_RAWAUX) if hard else uw.FMT_PALETTE
+        mats = []
+        for j, (shape) in enumerate((c["gate"], c["up"], c["down"])):
+            w = synth.weights(shape[0], shape[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"])
+            mats.append(uw.Matrix(w, fmt))
+            del w
+        distinct.append(mats)
+    log(f"stack: 4 distinct layers encoded in {time.perf_counter() - t0:.1f} s")
+    stack, pipes_easy_hard = [], []
+    for l in range(L):
+        for j in range(3):
+            src = distinct[l % 4][j]
+            stack.append(src if l < 4 else src.clone())
+            pipes_easy_hard.append(3 if l % 2 == 0 else 4)
+    resident = sum(m.info()["resident_bytes"] for m in stack)
+    # scratch: two slots per projection, alternating between hard layers
+    scratch = [[torch.empty(distinct[0][j].info()["scratch_bytes"][3], dtype=torch.uint8, device="cuda")
+                for j in range(3)] for _ in range(2)]
+    for l in range(0, L, 2):
+        for j in range(3):
+            stack[3 * l + j].set_scratch(scratch[(l // 2) % 2][j])
+    out = {"layers": L, "resident_GB": round(resident / 1e9, 2), "distinct_layers_generated": 4,
+           "hard": "even layers, Huffman + runtime palette transcode (P3)", "easy": "odd layers, direct palette (P4)"}
+    xs = synth.activations(max(tokens_list), hidden, xseed=1)
+    for tokens in tokens_list:
+        x = uw.bf16_tensor(xs[:tokens])
+        res = tune_split(torch, stack, pipes_easy_hard, x, tokens, [0, 32, 64, 128], steps=steps, log=log)
+        best_ms, best_split = res[0]
+        serial = [ms for ms, n in res if n == 0][0]
+        # all layers read as direct palette would need palette copies of the hard layers; time instead the
+        # uncompressed bf16 stack: 4 distinct bf16 layers cycled (each 1.4 GB, no cache reuse across layers)
+        wd = [[uw.bf16_tensor(synth.weights(sh[0], sh[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"]))
+               for j, sh in enumerate((c["gate"], c["up"], c["down"]))] for l in range(2)]
+        g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
+        u = torch.empty_like(g)
+        h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
+        yb = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        st = torch.cuda.Stream()
+
+        def bf16_pass():
+            for l in range(L):
+                wl = wd[l % 2]
+                uw.gemm_bf16(x, wl[0], g, tokens, inter, hidden, st)
+                uw.gemm_bf16(x, wl[1], u, tokens, inter, hidden, st)
+                uw.silu_mul(g, u, h, st)
+                uw.gemm_bf16(h, wl[2], yb, tokens, hidden, inter, st)
+        bms = time_graph(torch, bf16_pass, 2, 1, st, use_graph=False)
+        del wd
+        torch.cuda.empty_cache()
+        out[str(tokens)] = {"serial_us": round(serial * 1e3, 1), "overlap_best_us": round(best_ms * 1e3, 1),
+                            "best_side_cus": best_split, "splits": {str(n): round(ms * 1e3, 1) for ms, n in res},
+                            "bf16_hipblaslt_us": round(bms * 1e3, 1),
+                            "weight_GB_per_pass_bf16": round(2 * 3 * L * hidden * inter / 1e9, 1)}
+        log("stack", tokens, json.dumps(out[str(tokens)]))
+    for m in stack:
+        m.free()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +256,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
+    ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
+    ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -326,6 +375,29 @@ def main() -> int:
     }
     if args.sweep:
         result["sweep"] = sweep(torch, uw, synth, stream, args.steps, args.warmup)
+    if args.tune:
+        from decode_gemm_bf16_amd import tune as T
+        c8 = synth.CONFIGS["mlp_8b"]
+        layer = {}
+        for proj in T.PROJECTIONS:
+            rr, cc, sd = c8[proj]
+            m = uw.Matrix(synth.weights(rr, cc, sd, c8["p"], c8["shift"]), uw.FMT_HUFFMAN | uw.FMT_PALETTE)
+            layer[proj] = T.copies_for(m, 1 << 30)
+            for mm in layer[proj]:
+                mm.set_streams(stream)
+        nmin = min(len(v) for v in layer.values())
+        layer = {k: v[:nmin] for k, v in layer.items()}
+        result["tune"] = T.tune_mlp(torch, layer, [1, 16, 64, 256, 1024], stream, keep=3, log=log)
+        for v in layer.values():
+            for m in v:
+                m.free()
+        torch.cuda.empty_cache()
+    if args.stack:
+        for m in mats:
+            m.free()
+        mats = []
+        torch.cuda.empty_cache()
+        result["stack"] = stack_bench(torch, uw, synth, [1, 256], steps=2)
     if not args.no_cpu:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, x_bits, args.cpu_seconds)

@@ -47,7 +47,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   const int lo = (int)(((int64_t)blockIdx.y * kbn) / ksplit);
   const int hi = (int)(((int64_t)(blockIdx.y + 1) * kbn) / ksplit);
   const size_t brick_row0 = (size_t)blockIdx.x * kbn;
-  const uint32_t lut[4] = {in_vgpr(lut0), in_vgpr(lut1), in_vgpr(lut2), in_vgpr(lut3)};
+  const uint32_t lut[4] = {lut0, lut1, lut2, lut3};  // scalar: registers are scarce here
   constexpr int STEP = WAVES * U;
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
@@ -65,9 +65,9 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
     xlane[t] = ((uint32_t)tok * cols + q * 16) * 2;
   }
 
-  f32x4 acc[TB], acc2[TB];
+  f32x4 acc[TB];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) acc[t] = acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // per-brick table of the stage that will be fetched next
   uint2 mnext[U];
@@ -130,13 +130,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
       }
       const bf16x8 a0 = as_bf16x8(w0);
       const bf16x8 a1 = as_bf16x8(w1);
-      // the two k-halves go to separate accumulators (no back-to-back dependency)
 #pragma unroll
-      for (int t = 0; t < TB; ++t)
+      for (int t = 0; t < TB; ++t) {
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(st.x[u][t][0]), acc[t], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < TB; ++t)
-        acc2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[u][t][1]), acc2[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[u][t][1]), acc[t], 0, 0, 0);
+      }
     }
   };
 
@@ -160,7 +158,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   // D layout of the 16x16 result: lane l holds rows 4*(l/16)+0..3, column l%16.
   __shared__ f32x4 red[WAVES][TB][64];
 #pragma unroll
-  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t] + acc2[t];
+  for (int t = 0; t < TB; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
   for (int i = threadIdx.x; i < TB * 64; i += WAVES * 64) {
     const int t = i >> 6, l = i & 63;
