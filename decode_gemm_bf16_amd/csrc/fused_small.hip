@@ -56,33 +56,36 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
   // per-lane byte offsets, fixed for the whole kernel
   const uint32_t lane16 = lane * 16, lane8 = lane * 8;
+  // Lanes of tokens past the batch read at an offset past every buffer's
+  // range: a buffer load there returns zeros and touches no memory.  Every
+  // load is then issued unconditionally, so the compiler can count the loads
+  // in flight and wait for one stage only, not for all of them.
   uint32_t xlane[TB];
-  bool xlive[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int tok = t * 16 + r;
-    xlive[t] = tok < tokens;
-    xlane[t] = ((uint32_t)tok * cols + q * 16) * 2;
+    xlane[t] = tok < tokens ? ((uint32_t)tok * cols + q * 16) * 2 : kOffRange;
   }
 
   f32x4 acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-brick table of the stage that will be fetched next
+  // per-brick table of the stage that will be fetched next (scalar loads)
   uint2 mnext[U];
   auto load_meta = [&](int kb0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + u * WAVES;
-      mnext[u] = (!EXPM && kb < hi) ? meta[brick_row0 + kb] : uint2{0u, 0u};
+      const int kb = min(kb0 + u * WAVES, hi - 1);
+      mnext[u] = EXPM ? uint2{0u, 0u} : meta[brick_row0 + kb];
     }
   };
+  // A stage past the slice's end re-reads its last brick (the compute step
+  // skips it), which keeps the number of loads per stage fixed.
   auto fetch = [&](Stage<U, TB, EXPM>& st, int kb0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = kb0 + u * WAVES;
-      if (kb >= hi) break;
+      const int kb = min(kb0 + u * WAVES, hi - 1);
       const uint32_t b = (uint32_t)brick_row0 + kb;
       st.s[u] = ld16(rs_sm, lane16, b * 1024);
       if (EXPM) {
@@ -92,19 +95,13 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
         const uint32_t map = mnext[u].x;
         st.anyraw[u] = map;
         st.raw[u] = (map >> r) & 1u;
-        if (map && st.raw[u]) {
-          const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-          st.e[u] = ld16(rs_side, (mnext[u].y + rank) * 64 + q * 16, 0);
-        }
+        const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
+        st.e[u] = ld16(rs_side, st.raw[u] ? (mnext[u].y + rank) * 64 + q * 16 : kOffRange, 0);
       }
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
-        st.x[u][t][0] = u32x4{0u, 0u, 0u, 0u};
-        st.x[u][t][1] = u32x4{0u, 0u, 0u, 0u};
-        if (xlive[t]) {
-          st.x[u][t][0] = ld16(rs_x, xlane[t], kb * 128);
-          st.x[u][t][1] = ld16(rs_x, xlane[t] + 16, kb * 128);
-        }
+        st.x[u][t][0] = ld16(rs_x, xlane[t], kb * 128);
+        st.x[u][t][1] = ld16(rs_x, xlane[t] + 16, kb * 128);
       }
     }
   };
@@ -144,12 +141,12 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   fetch(sa, kb);
   load_meta(kb + STEP);
   while (kb < hi) {
-    if (kb + STEP < hi) fetch(sb, kb + STEP);
+    fetch(sb, kb + STEP);
     load_meta(kb + 2 * STEP);
     compute(sa, kb);
     kb += STEP;
     if (kb >= hi) break;
-    if (kb + STEP < hi) fetch(sa, kb + STEP);
+    fetch(sa, kb + STEP);
     load_meta(kb + 2 * STEP);
     compute(sb, kb);
     kb += STEP;
@@ -179,6 +176,155 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   }
 }
 
+// Few tokens whose activations fit in LDS (tokens x cols <= kGemvX): the same
+// brick-row-per-workgroup split, arranged so that each wave keeps only weight
+// bytes in its load pipeline.  At the start the workgroup copies x and its
+// brick-row's per-brick table into LDS (all loads issued before the one wait),
+// so a brick costs three buffer loads: sign+mantissa, codes and the raw
+// side-table bytes (lanes of rows that are not raw read past the buffer's end,
+// which returns zeros without touching memory; issuing the load on every
+// brick keeps the load count per stage fixed, so waits cover one stage only).
+// Each wave runs a ring of D stages; the B operand comes from LDS at compute
+// time; partial sums are reduced one output per thread.
+constexpr int kGemvX = 16384;     // bf16 elements of x held in LDS
+constexpr int kGemvKbn = 1024;    // brick columns whose table fits the LDS copy
+
+struct GStage {
+  u32x4 s;       // sign+mantissa bytes
+  u32x4 e;       // raw side-table bytes (zeros for rows that are not raw)
+  u32x2 n;       // 4-bit codes
+  uint32_t map;  // wave-uniform raw-row map of the brick
+};
+
+template <int WAVES, int D>
+__global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
+    const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
+    const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
+    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int kbn = cols >> 6;
+  const uint32_t brick_row0 = blockIdx.x * (uint32_t)kbn;
+  const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
+  const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
+  const rsrc_t rs_sm = make_rsrc(sm, nweights);
+  const rsrc_t rs_codes = make_rsrc(codes, nweights / 2);
+  const rsrc_t rs_side = make_rsrc(side, side_bytes);
+  const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
+  const uint32_t lane16 = lane * 16, lane8 = lane * 8;
+  const bool live = r < tokens;
+  // LDS: x (tokens x cols bf16), a 32-byte zero tail read by lanes of absent
+  // tokens, then the brick-row's per-brick table
+  extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
+  const uint32_t xbytes = (uint32_t)tokens * cols * 2;
+  uint2* ms = (uint2*)(gemv_lds + xbytes + 32);
+  const uint32_t xl_lane = live ? ((uint32_t)r * cols + q * 16) * 2 : xbytes;
+  const uint32_t xl_step = live ? 128u : 0u;
+
+  const int nmine = (kbn - wave + WAVES - 1) / WAVES;  // bricks kb = wave + WAVES*i of this wave
+  auto fetch = [&](GStage& st, int i, bool table_in_lds) {
+    i = min(i, nmine - 1);  // a stage past the end re-reads the last brick; compute skips it
+    const int kb = wave + WAVES * i;
+    const uint2 m = table_in_lds ? ms[kb] : meta[brick_row0 + kb];
+    const uint32_t map = __builtin_amdgcn_readfirstlane(m.x);
+    const uint32_t before = __builtin_amdgcn_readfirstlane(m.y);
+    const uint32_t b = brick_row0 + kb;
+    st.s = ld16(rs_sm, lane16, b * 1024);
+    st.n = ld8(rs_codes, lane8, b * 512);
+    st.map = map;
+    const bool raw = (map >> r) & 1u;
+    const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
+    st.e = ld16(rs_side, raw ? (before + rank) * 64 + q * 16 : kOffRange, 0);
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const GStage& st, int i) {
+    const int kb = wave + WAVES * i;
+    const u32x4* p = (const u32x4*)(gemv_lds + xl_lane + kb * xl_step);
+    const u32x4 xb0 = p[0], xb1 = p[1];
+    uint32_t v[4];
+    palette_v(st.n, lut, v);
+    if (st.map) {  // wave-uniform: the brick holds a raw group
+      if ((st.map >> r) & 1u) {
+        v[0] = rot_exp(st.e.x);
+        v[1] = rot_exp(st.e.y);
+        v[2] = rot_exp(st.e.z);
+        v[3] = rot_exp(st.e.w);
+      }
+    }
+    u32x4 w0, w1;
+    rebuild_v2(st.s, v, w0, w1);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(xb0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(xb1), acc, 0, 0, 0);
+  };
+
+  GStage st[D];
+  if (nmine > 0) {  // the first stages read the table from global memory (scalar loads)
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch(st[j], j, false);
+  }
+  {
+    constexpr int NT = WAVES * 64;
+    constexpr int NXV = (kGemvX / 8 + NT - 1) / NT, NMV = (kGemvKbn + NT - 1) / NT;
+    const rsrc_t rs_meta = make_rsrc(meta + brick_row0, (uint64_t)kbn * 8);
+    const int n16 = tokens * cols / 8;
+    u32x4 xv[NXV];
+    u32x2 mv[NMV];
+#pragma unroll
+    for (int k = 0; k < NMV; ++k) {
+      const int i = threadIdx.x + k * NT;
+      mv[k] = ld8(rs_meta, i < kbn ? i * 8 : kOffRange, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      const int i = threadIdx.x + k * NT;
+      xv[k] = ld16(rs_x, i < n16 ? i * 16 : kOffRange, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NMV; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < kbn) ms[i] = uint2{mv[k].x, mv[k].y};
+    }
+#pragma unroll
+    for (int k = 0; k < NXV; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < n16) ((u32x4*)gemv_lds)[i] = xv[k];
+    }
+    if (threadIdx.x < 2) ((u32x4*)(gemv_lds + xbytes))[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+  }
+  for (int i = 0; i < nmine; i += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (i + j < nmine) compute(st[j], i + j);
+      fetch(st[j], i + j + D, true);
+    }
+  }
+
+  // partial sums of all waves; each output summed by one thread, waves in order
+  __shared__ float red[WAVES][256];
+  *(f32x4*)&red[wave][lane * 4] = acc;
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += WAVES * 64) {
+    const int l = i >> 2, j = i & 3;
+    const int tok = l & 15;  // D layout: lane l holds rows 4*(l/16)+0..3 of column (token) l%16
+    if (tok >= tokens) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += red[w][i];
+    y[(size_t)tok * rows + (size_t)blockIdx.x * 16 + 4 * (l >> 4) + j] = sum;
+  }
+}
+
+template <int WAVES, int D>
+hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, hipStream_t s) {
+  const size_t lds = (size_t)tokens * w.cols * 2 + 32 + (size_t)(w.cols / 64) * 8;
+  hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s, w.sm,
+                     w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
+                     (int)tokens, (int)w.rows, (int)w.cols);
+  return hipGetLastError();
+}
+
 template <int WAVES, int TB, bool EXPM, int U>
 hipError_t launch_one(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int ksplit, hipStream_t s) {
   dim3 grid((unsigned)(w.rows / 16), (unsigned)ksplit);
@@ -205,6 +351,20 @@ hipError_t launch_tb(const FusedW& w, const uint16_t* x, float* y, int64_t token
 }
 
 }  // namespace
+
+bool gemv_applies(const FusedW& w, int64_t tokens) {
+  return !w.exp_mode && tokens >= 1 && tokens <= 16 && tokens * w.cols <= kGemvX && w.cols / 64 <= kGemvKbn;
+}
+
+hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                             hipStream_t s) {
+  if (!gemv_applies(w, tokens)) return hipErrorInvalidValue;
+#define UW_CASE(W, D) \
+  if (v.waves == W && v.unroll == D) return launch_gemv<W, D>(w, x, y, tokens, s);
+  UW_CASE(8, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)
+#undef UW_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_fused_small(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                               hipStream_t s) {

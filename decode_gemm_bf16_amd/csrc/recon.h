@@ -132,6 +132,10 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 // arithmetic, and the per-lane part of an offset is computed once per kernel.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+// A per-lane offset past every range make_rsrc sets: the buffer unit's range
+// check turns such a load into zeros without a memory access.
+constexpr uint32_t kOffRange = 0x80000000u;
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);

@@ -12,6 +12,9 @@ hipError_t launch_fused_small(const FusedW& w, const uint16_t* x, float* y, int6
                               hipStream_t s);
 hipError_t launch_fused_large(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                               hipStream_t s);
+hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                             hipStream_t s);
+bool gemv_applies(const FusedW& w, int64_t tokens);
 
 namespace {
 
@@ -20,7 +23,7 @@ struct Named {
   const char* name;
 };
 
-// small batch: kind 0, {waves, ksplit, unroll}
+// small batch: kind 0, {waves, ksplit, unroll}; kind 2, {waves, -, ring depth}
 const Named kSmall[] = {
     {{0, 8, 1, 2, 0}, "small:w8:k1:u2"},  {{0, 4, 1, 2, 0}, "small:w4:k1:u2"},
     {{0, 16, 1, 1, 0}, "small:w16:k1:u1"}, {{0, 8, 1, 4, 0}, "small:w8:k1:u4"},
@@ -28,6 +31,9 @@ const Named kSmall[] = {
     {{0, 8, 4, 2, 0}, "small:w8:k4:u2"},  {{0, 4, 2, 2, 0}, "small:w4:k2:u2"},
     {{0, 16, 1, 2, 0}, "small:w16:k1:u2"}, {{0, 4, 4, 2, 0}, "small:w4:k4:u2"},
     {{0, 8, 1, 1, 0}, "small:w8:k1:u1"},  {{0, 4, 4, 4, 0}, "small:w4:k4:u4"},
+    // x held in LDS (palette forms, tokens x cols <= 16384); {waves, ring depth}
+    {{2, 8, 1, 2, 0}, "gemv:w8:d2"},      {{2, 16, 1, 2, 0}, "gemv:w16:d2"},
+    {{2, 8, 1, 3, 0}, "gemv:w8:d3"},      {{2, 4, 1, 3, 0}, "gemv:w4:d3"},
 };
 // large batch: kind 1, {tile, ksplit}
 const Named kLarge[] = {
@@ -59,14 +65,27 @@ const char* variant_name(int64_t tokens, int id) {
 
 // Built-in choice when no plan is set (measured on MI355X with the 8B-shaped
 // projections; the autotuner refines it per matrix and batch).
+namespace {
+
+Variant small_default(int64_t tokens, int64_t rows, int64_t cols) {
+  const int64_t brows = rows / 16, kbn = cols / 64;
+  // one 16-row brick-row per workgroup already gives >= 4096 waves for the
+  // 4096-row down projection; K is split only for very short matrices
+  Variant v{0, tokens <= 16 ? 16 : 8, 1, 1, 0};
+  if (brows < 128) v.ksplit = (int)std::min<int64_t>({8, (256 + brows - 1) / brows, kbn});
+  return v;
+}
+
+}  // namespace
+
 Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   const int64_t brows = rows / 16, kbn = cols / 64;
   if (tokens <= 64) {
-    // one 16-row brick-row per workgroup already gives >= 4096 waves for the
-    // 4096-row down projection; K is split only for very short matrices
-    Variant v{0, tokens <= 16 ? 16 : 8, 1, 1, 0};
-    if (brows < 128) v.ksplit = (int)std::min<int64_t>({8, (256 + brows - 1) / brows, kbn});
-    return v;
+    // activations in LDS when they fit and there are enough brick-rows to
+    // fill the chip without splitting K (the launch falls back to the small
+    // kernel for the exponent form)
+    if (tokens <= 16 && tokens * cols <= 16384 && kbn <= 1024 && brows >= 128) return Variant{2, 8, 1, 2, 0};
+    return small_default(tokens, rows, cols);
   }
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
@@ -85,6 +104,12 @@ hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t to
   Variant v = v0;
   v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, w.cols / 64));
   if (tokens <= 64) {
+    if (v.kind == 2) {
+      // x in LDS where it fits; elsewhere (exponent form, more activations)
+      // the same choice falls back to the small kernel's default shape
+      if (gemv_applies(w, tokens)) return launch_fused_gemv(w, x, y, tokens, v, s);
+      v = small_default(tokens, w.rows, w.cols);
+    }
     if (v.kind != 0) return hipErrorInvalidValue;
     return launch_fused_small(w, x, y, tokens, v, s);
   }
