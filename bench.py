@@ -37,8 +37,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "fused decode+GEMM eff. weight GB/s & TFLOP/s at batch 1–1024; bits/weight"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_small_gate_b1_traffic.txt")
-KERNEL_SOURCES = ["decode_gemm_bf16_amd/csrc/fused_small.hip", "decode_gemm_bf16_amd/csrc/recon.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_gemv_gate_b1_traffic.txt")
+# sources that decide which kernel the headline runs and what it reads
+KERNEL_SOURCES = ["decode_gemm_bf16_amd/csrc/fused_small.hip", "decode_gemm_bf16_amd/csrc/recon.h",
+                  "decode_gemm_bf16_amd/csrc/variants.cpp", "decode_gemm_bf16_amd/csrc/kernels.h"]
 
 
 def time_graph(torch, fn, steps, warmup, stream, use_graph=True):
@@ -55,6 +57,19 @@ def kernel_sha() -> str:
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_label(name: str, tokens: int) -> str:
+    """The name rocprofv3 gives (template arguments included) to the fused
+    kernel that a small-batch variant launches."""
+    import re
+    m = re.match(r"gemv:w(\d+):d(\d+)", name)
+    if m:
+        return f"fused_gemv_kernel<{m[1]}, {m[2]}>"
+    m = re.match(r"small:w(\d+):k\d+:u(\d+)", name)
+    if m:
+        return f"fused_small_kernel<{m[1]}, {min(4, (tokens + 15) // 16)}, false, {m[2]}>"
+    return name
 
 
 def cpu_baseline(w, x, seconds: float) -> dict:
@@ -333,6 +348,7 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     traffic = load_traffic()
+    _, in_use = mats[0].variant_in_use(tokens, uw.P4_DIRECT_PALETTE)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -351,13 +367,13 @@ def main() -> int:
             "rows": rows, "cols": cols, "tokens": tokens, "pipeline": "P4 direct palette",
             "bits_per_weight": round(pinfo["bpw_palette"], 4),
             "weight_byte_reduction": round(1 - pinfo["bpw_palette"] / 16, 4),
-            "copies_rotated": ncopy, "variant": uw.variant_name(tokens, args.variant),
+            "copies_rotated": ncopy, "variant": in_use,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(algo_bytes), "avg_launch_us": round(ms * 1e3, 3),
-            "kernel": "fused_small_kernel<8,1,false,2>", "kernel_sha": kernel_sha(),
+            "kernel": kernel_label(in_use, tokens), "kernel_sha": kernel_sha(),
         },
         "extra": {
             "tflops": round(2.0 * n * tokens / t_s / 1e12, 4),

@@ -26,7 +26,7 @@ FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 
 EXPORTED = [
     "uw_encode", "uw_decode", "uw_matmul", "uw_preprocess", "uw_set_streams", "uw_set_scratch", "uw_set_plan",
-    "uw_set_variant", "uw_variant_name", "uw_query", "uw_export", "uw_clone", "uw_free", "uw_last_error", "uw_silu_mul",
+    "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_free", "uw_last_error", "uw_silu_mul",
     "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_stack_forward", "uw_stack_workspace_bytes",
     "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy", "uw_device_read",
 ]
@@ -80,6 +80,7 @@ def _load() -> C.CDLL:
         "uw_set_plan": ([vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32), i32], st),
         "uw_set_variant": ([vp, i32], st),
         "uw_variant_name": ([i64, i32], C.c_char_p),
+        "uw_variant_in_use": ([vp, i64, i32, C.POINTER(i32), C.c_char_p, C.c_size_t], st),
         "uw_query": ([vp, C.POINTER(Info)], st),
         "uw_export": ([vp, C.c_int, vp, C.c_size_t, C.POINTER(C.c_size_t)], st),
         "uw_clone": ([vp, C.POINTER(vp)], st),
@@ -212,6 +213,13 @@ class Matrix:
 
     def set_variant(self, variant: int) -> None:
         _check(_lib.uw_set_variant(self._h, variant))
+
+    def variant_in_use(self, tokens: int, pipeline: int = 0) -> tuple[int, str]:
+        """(pipeline, variant name) that matmul(..., tokens, pipeline) would run."""
+        p = C.c_int32(0)
+        buf = C.create_string_buffer(96)
+        _check(_lib.uw_variant_in_use(self._h, tokens, pipeline, C.byref(p), buf, 96))
+        return p.value, buf.value.decode()
 
     def info(self) -> dict:
         inf = Info()

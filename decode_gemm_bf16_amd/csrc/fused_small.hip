@@ -186,8 +186,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
 // brick keeps the load count per stage fixed, so waits cover one stage only).
 // Each wave runs a ring of D stages; the B operand comes from LDS at compute
 // time; partial sums are reduced one output per thread.
-constexpr int kGemvX = 16384;     // bf16 elements of x held in LDS
-constexpr int kGemvKbn = 1024;    // brick columns whose table fits the LDS copy
+constexpr int kGemvX = (int)kGemvXElems;   // bf16 elements of x held in LDS
+constexpr int kGemvKbn = (int)kGemvKbnMax;  // brick columns whose table fits the LDS copy
 
 struct GStage {
   u32x4 s;       // sign+mantissa bytes
@@ -352,13 +352,10 @@ hipError_t launch_tb(const FusedW& w, const uint16_t* x, float* y, int64_t token
 
 }  // namespace
 
-bool gemv_applies(const FusedW& w, int64_t tokens) {
-  return !w.exp_mode && tokens >= 1 && tokens <= 16 && tokens * w.cols <= kGemvX && w.cols / 64 <= kGemvKbn;
-}
-
 hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                              hipStream_t s) {
-  if (!gemv_applies(w, tokens)) return hipErrorInvalidValue;
+  if (w.exp_mode || tokens < 1 || tokens > 16 || tokens * w.cols > kGemvX || w.cols / 64 > kGemvKbn)
+    return hipErrorInvalidValue;
 #define UW_CASE(W, D) \
   if (v.waves == W && v.unroll == D) return launch_gemv<W, D>(w, x, y, tokens, s);
   UW_CASE(8, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)

@@ -33,7 +33,16 @@ struct Variant {
 int variant_count(int64_t tokens);
 bool variant_get(int64_t tokens, int id, Variant* v);  // id 0 = default for (tokens, shape)
 Variant variant_default(int64_t tokens, int64_t rows, int64_t cols);
+// The variant that actually launches for v (a choice that does not apply to
+// the shape or form falls back to the default of its family).
+Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_mode, const Variant& v);
+// Activations kept in LDS by the gemv variants: tokens x cols <= kGemvXElems
+// bf16 and at most kGemvKbnMax 64-column bricks per row.
+constexpr int64_t kGemvXElems = 16384;
+constexpr int64_t kGemvKbnMax = 1024;
 const char* variant_name(int64_t tokens, int id);
+// Name of a variant (its list entry, else a description of its fields).
+void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len);
 
 hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                         hipStream_t s);

@@ -528,6 +528,27 @@ uw_status uw_set_variant(uw_handle h, int32_t variant) {
 
 const char* uw_variant_name(int64_t tokens, int32_t variant) { return uw::variant_name(tokens, variant); }
 
+uw_status uw_variant_in_use(uw_handle h, int64_t tokens, int32_t pipeline, int32_t* pipeline_out, char* name,
+                            size_t name_len) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
+  int var = 0;
+  const int p = resolve_pipeline(h, tokens, pipeline, &var);
+  uw_status st = check_pipeline(h, p);
+  if (st != UW_OK) return st;
+  uw::Variant v = uw::variant_default(tokens, h->rows, h->cols);
+  if (var != 0 && !uw::variant_get(tokens, var, &v))
+    return fail(UW_ERR_INVALID_ARG, "variant %d does not exist for %lld tokens", var, (long long)tokens);
+  if (pipeline_out) *pipeline_out = p;
+  if (name && name_len) {
+    if (p == 1)
+      snprintf(name, name_len, "hipblaslt");
+    else
+      uw::variant_describe(tokens, uw::variant_effective(tokens, h->rows, h->cols, p == 2, v), name, name_len);
+  }
+  return UW_OK;
+}
+
 uw_status uw_query(uw_handle h, uw_info* o) {
   if (!h || !o) return fail(UW_ERR_INVALID_ARG, "null argument");
   std::memset(o, 0, sizeof *o);

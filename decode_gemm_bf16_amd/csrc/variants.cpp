@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 
 #include "kernels.h"
 
@@ -14,7 +15,6 @@ hipError_t launch_fused_large(const FusedW& w, const uint16_t* x, float* y, int6
                               hipStream_t s);
 hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                              hipStream_t s);
-bool gemv_applies(const FusedW& w, int64_t tokens);
 
 namespace {
 
@@ -43,6 +43,17 @@ const Named kLarge[] = {
     {{1, 0, 2, 0, 1}, "large:t1(4x32r x128t):k2"}, {{1, 0, 1, 0, 2}, "large:t2(2x64r x128t):k1"},
     {{1, 0, 2, 0, 2}, "large:t2(2x64r x128t):k2"}, {{1, 0, 1, 0, 3}, "large:t3(4x64r x64t):k1"},
     {{1, 0, 2, 0, 3}, "large:t3(4x64r x64t):k2"},
+    // 32x32x16 instructions
+    {{1, 0, 1, 0, 4}, "large:t4(4x64r x128t,32x32):k1"}, {{1, 0, 2, 0, 4}, "large:t4(4x64r x128t,32x32):k2"},
+    {{1, 0, 4, 0, 4}, "large:t4(4x64r x128t,32x32):k4"}, {{1, 0, 1, 0, 5}, "large:t5(4x32r x128t,32x32):k1"},
+    {{1, 0, 2, 0, 5}, "large:t5(4x32r x128t,32x32):k2"}, {{1, 0, 1, 0, 6}, "large:t6(2x64r x128t,32x32):k1"},
+    {{1, 0, 1, 0, 7}, "large:t7(4x64r x64t,32x32):k1"},  {{1, 0, 2, 0, 7}, "large:t7(4x64r x64t,32x32):k2"},
+    {{1, 0, 1, 0, 8}, "large:t8(4x64r x256t,32x32):k1"}, {{1, 0, 2, 0, 8}, "large:t8(4x64r x256t,32x32):k2"},
+    {{1, 0, 1, 0, 9}, "large:t9(4x32r x256t,32x32):k1"}, {{1, 0, 2, 0, 9}, "large:t9(4x32r x256t,32x32):k2"},
+    {{1, 0, 1, 0, 10}, "large:t10(4x64r x256t,32x32,interleaved):k1"},
+    {{1, 0, 2, 0, 10}, "large:t10(4x64r x256t,32x32,interleaved):k2"},
+    {{1, 0, 1, 0, 11}, "large:t11(4x64r x256t,32x32,interleaved,B groups):k1"},
+    {{1, 0, 2, 0, 11}, "large:t11(4x64r x256t,32x32,interleaved,B groups):k2"},
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -61,6 +72,25 @@ const char* variant_name(int64_t tokens, int id) {
   if (id == 0) return tokens <= 64 ? "small:default" : "large:default";
   if (id < 0 || id >= variant_count(tokens)) return nullptr;
   return tokens <= 64 ? kSmall[id - 1].name : kLarge[id - 1].name;
+}
+
+void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len) {
+  if (!buf || len == 0) return;
+  const Named* list = tokens <= 64 ? kSmall : kLarge;
+  const int n = tokens <= 64 ? kNSmall : kNLarge;
+  for (int i = 0; i < n; ++i) {
+    const Variant& u = list[i].v;
+    if (u.kind == v.kind && u.waves == v.waves && u.ksplit == v.ksplit && u.unroll == v.unroll && u.tile == v.tile) {
+      snprintf(buf, len, "%s", list[i].name);
+      return;
+    }
+  }
+  if (v.kind == 1)
+    snprintf(buf, len, "large:t%d:k%d", v.tile, v.ksplit);
+  else if (v.kind == 2)
+    snprintf(buf, len, "gemv:w%d:d%d", v.waves, v.unroll);
+  else
+    snprintf(buf, len, "small:w%d:k%d:u%d", v.waves, v.ksplit, v.unroll);
 }
 
 // Built-in choice when no plan is set (measured on MI355X with the 8B-shaped
@@ -84,32 +114,42 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // activations in LDS when they fit and there are enough brick-rows to
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
-    if (tokens <= 16 && tokens * cols <= 16384 && kbn <= 1024 && brows >= 128) return Variant{2, 8, 1, 2, 0};
+    if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128) return Variant{2, 8, 1, 2, 0};
     return small_default(tokens, rows, cols);
   }
+  // 256 x 256 tiles with the rebuild interleaved into the MFMAs once there are
+  // enough tokens to fill the chip with them (one workgroup per CU)
+  const int64_t wg11 = ((brows + 15) / 16) * ((tokens + 255) / 256);
+  if (tokens >= 512 && wg11 >= 192) return Variant{1, 0, 1, 0, 11};
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
-  const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tile 1: 128 rows per workgroup
+  const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tiles 1/5: 128 rows per workgroup
   Variant v{1, 0, 1, 0, wg0 >= 384 ? 0 : 1};
   const int64_t wgs = v.tile == 0 ? wg0 : wg1;
   if (wgs < 128)
     v.ksplit = (int)std::min<int64_t>({8, (256 + wgs - 1) / wgs, kbn});
   else if (wgs < 384 && kbn >= 128)
     v.ksplit = 2;
+  if (v.tile == 1 && v.ksplit == 1) v.tile = 5;  // same tile on 32x32x16 instructions
+  return v;
+}
+
+Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_mode, const Variant& v0) {
+  Variant v = v0;
+  v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, cols / 64));
+  // x in LDS where it fits; elsewhere (exponent form, more activations) the
+  // same choice falls back to the small kernel's default shape
+  if (tokens <= 64 && v.kind == 2 &&
+      !(!exp_mode && tokens <= 16 && tokens * cols <= kGemvXElems && cols / 64 <= kGemvKbnMax))
+    v = small_default(tokens, rows, cols);
   return v;
 }
 
 hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v0,
                         hipStream_t s) {
-  Variant v = v0;
-  v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, w.cols / 64));
+  const Variant v = variant_effective(tokens, w.rows, w.cols, w.exp_mode, v0);
   if (tokens <= 64) {
-    if (v.kind == 2) {
-      // x in LDS where it fits; elsewhere (exponent form, more activations)
-      // the same choice falls back to the small kernel's default shape
-      if (gemv_applies(w, tokens)) return launch_fused_gemv(w, x, y, tokens, v, s);
-      v = small_default(tokens, w.rows, w.cols);
-    }
+    if (v.kind == 2) return launch_fused_gemv(w, x, y, tokens, v, s);
     if (v.kind != 0) return hipErrorInvalidValue;
     return launch_fused_small(w, x, y, tokens, v, s);
   }

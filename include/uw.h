@@ -164,6 +164,15 @@ uw_status uw_set_variant(uw_handle h, int32_t variant);
 /* Name of fused-kernel variant `variant` for `tokens`, or NULL past the end. */
 const char* uw_variant_name(int64_t tokens, int32_t variant);
 
+/* What uw_matmul(h, ..., tokens, pipeline) would run, without running it:
+ * *pipeline_out (if not NULL) receives the pipeline after plan / built-in
+ * resolution, and `name` (capacity name_len bytes, NUL-terminated; may be
+ * NULL) the fused-kernel variant's name as listed by uw_variant_name (or
+ * "hipblaslt" for pipeline 1, whose matmul is the library GEMM).  Errors as
+ * uw_matmul for an unusable pipeline or variant.  Host only: no GPU work. */
+uw_status uw_variant_in_use(uw_handle h, int64_t tokens, int32_t pipeline, int32_t* pipeline_out, char* name,
+                            size_t name_len);
+
 uw_status uw_query(uw_handle h, uw_info* out);
 
 /* Copy one stored stream to host memory `dst` (capacity `cap` bytes);

@@ -131,6 +131,32 @@ def test_variant_names():
     assert uw.variant_name(1, 999) is None
 
 
+def test_variant_in_use_resolution():
+    """Which pipeline and kernel shape a call would run (no GPU work): the
+    built-in rule, the exponent-form fallback of the LDS-activation shapes,
+    an explicit variant and a plan."""
+    m = uw.Matrix(synth.weights(2048, 4096, 1, 0.0005, 10), HOST_ALL)
+    assert m.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d2")
+    assert m.variant_in_use(1, uw.P1_FULL_DECODE)[1] == "hipblaslt"
+    # the exponent form has no palette codes: the small kernel runs instead
+    p, name = m.variant_in_use(1, uw.P2_EXP_DECODE)
+    assert p == uw.P2_EXP_DECODE and name.startswith("small:")
+    # 5 tokens x 4096 columns no longer fit the LDS activation buffer
+    assert m.variant_in_use(5)[1].startswith("small:")
+    assert m.variant_in_use(1024)[1].startswith("large:")
+    v = uw.variants(1).index("small:w8:k1:u2")
+    m.set_variant(v)
+    assert m.variant_in_use(1, uw.P4_DIRECT_PALETTE) == (uw.P4_DIRECT_PALETTE, "small:w8:k1:u2")
+    m.set_variant(0)
+    # a plan selects pipeline and variant per batch size
+    m.set_plan([(16, uw.P1_FULL_DECODE, 0), (1 << 30, uw.P4_DIRECT_PALETTE, v)])
+    assert m.variant_in_use(1) == (uw.P1_FULL_DECODE, "hipblaslt")
+    assert m.variant_in_use(17) == (uw.P4_DIRECT_PALETTE, "small:w8:k1:u2")
+    with pytest.raises(uw.UwError) as e:
+        uw.Matrix(synth.weights(64, 64, 1, 0.0, 0), uw.FMT_PALETTE | uw.ENC_HOST_ONLY).variant_in_use(1, uw.P1_FULL_DECODE)
+    assert e.value.status in (uw.ERR_UNSUPPORTED, uw.ERR_INVALID_ARG)
+
+
 def test_bits_per_weight_on_gate_shaped_slice():
     """North-star size target: >= 20% fewer weight bytes than bf16 in both forms."""
     w = synth.weights(1024, 4096, 0, 0.0005, 10)
