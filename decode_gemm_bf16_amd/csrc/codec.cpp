@@ -240,4 +240,23 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
   return std::string();
 }
 
+std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut) {
+  std::vector<uint32_t> out(kLutSize, 0);
+  for (uint32_t p = 0; p < uint32_t(kLutSize); ++p) {
+    uint32_t syms = 0, cnt = 0, pos = 0;
+    while (cnt < 3) {
+      // the code starting `pos` bits into the window (bits past the window read
+      // as zeros: only a code that ends inside the window is taken)
+      const uint16_t e = lut[(p << pos) & uint32_t(kLutSize - 1)];
+      const uint32_t len = e >> 8;
+      if (len == 0 || pos + len > uint32_t(kLmax)) break;
+      syms |= uint32_t(e & 0xFF) << (8 * cnt);
+      ++cnt;
+      pos += len;
+    }
+    out[p] = syms | (cnt << 24) | (pos << 26);
+  }
+  return out;
+}
+
 }  // namespace uw

@@ -54,6 +54,12 @@ struct HostFormat {
 std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t formats,
                         HostFormat& out);
 
+// Multi-symbol decode table: for each 12-bit window, the whole codes it
+// starts with, greedily and at most three: bits 0-23 the symbols (first in the
+// low byte), bits 24-25 their count (>= 1 for a complete code), bits 26-29
+// the bits they take.  Built from the one-symbol table `lut`.
+std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut);
+
 // Length-limited optimal code lengths over a 256-symbol histogram.
 void limited_code_lengths(const uint64_t hist[256], int lmax, uint8_t lengths[256]);
 

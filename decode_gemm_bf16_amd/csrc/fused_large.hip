@@ -36,7 +36,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    int ksplit, int n_tblk, int n_rblk) {
+    int ksplit, int n_tblk, int n_rblk, uint64_t codes_bytes, int codes_ilv) {
   constexpr int TOK = 16 * TBK;                    // tokens per workgroup
   constexpr int XCHUNKS = TOK * 8;                 // 16-byte pieces of one activation tile
   constexpr int XPER = XCHUNKS / (WAVES * 64);     // pieces per thread
@@ -74,10 +74,12 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large_kernel(
   const uint32_t lut[4] = {in_vgpr(lut0), in_vgpr(lut1), in_vgpr(lut2), in_vgpr(lut3)};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
-  const rsrc_t rs_codes = make_rsrc(codes, EXPM ? nweights : nweights / 2);
+  const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
-  const uint32_t lane16 = lane * 16, lane8 = lane * 8;
+  const uint32_t lane16 = lane * 16;
+  constexpr uint32_t CS = EXPM ? 16 : 8;  // code-stream bytes per run
+  const uint32_t clane = code_lane_off(q, r, CS, codes_ilv);
   // activation pieces this thread stages: token row and byte offset inside a K step
   uint32_t xoff[XPER];
   bool xlive[XPER];
@@ -124,9 +126,9 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large_kernel(
         const uint32_t b = (uint32_t)(brow0 + i) * kbn + kb;
         wr.s[i] = ld16(rs_sm, lane16, b * 1024);
         if (EXPM) {
-          wr.e[i] = ld16(rs_codes, lane16, b * 1024);
+          wr.e[i] = ld16(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
         } else {
-          wr.n[i] = ld8(rs_codes, lane8, b * 512);
+          wr.n[i] = ld8(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
           const uint32_t map = mnext[i].x;
           wr.anyraw[i] = map;
           wr.raw[i] = (map >> r) & 1u;
@@ -242,11 +244,11 @@ hipError_t launch_large_t(const FusedW& w, const uint16_t* x, float* y, int64_t 
   if (w.exp_mode)
     hipLaunchKernelGGL((fused_large_kernel<WAVES, RB, TBK, true>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                        w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
-                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   else
     hipLaunchKernelGGL((fused_large_kernel<WAVES, RB, TBK, false>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                        w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
-                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large32_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    int ksplit, int n_tblk, int n_rblk) {
+    int ksplit, int n_tblk, int n_rblk, uint64_t codes_bytes, int codes_ilv) {
   constexpr int TOK = 32 * TB2;                    // tokens per workgroup
   constexpr int XCHUNKS = TOK * 8;                 // 16-byte pieces of one activation tile
   constexpr int XPER = XCHUNKS / (WAVES * 64);     // pieces per thread
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large32_kernel(
   const uint32_t lut[4] = {in_vgpr(lut0), in_vgpr(lut1), in_vgpr(lut2), in_vgpr(lut3)};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
-  const rsrc_t rs_codes = make_rsrc(codes, EXPM ? nweights : nweights / 2);
+  const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
   // per-lane offsets of the lane's run inside brick-row brow0 + 2rb (rows past
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large32_kernel(
   for (int rb = 0; rb < RB2; ++rb) {
     const bool ok = brow0 + 2 * rb + pb < brows;
     voff_s[rb] = ok ? run * 16 + (uint32_t)pb * kbn * 1024 : kOffRange;
-    voff_n[rb] = ok ? run * (EXPM ? 16 : 8) + (uint32_t)pb * kbn * (EXPM ? 1024 : 512) : kOffRange;
+    voff_n[rb] = ok ? 0u : kOffRange;  // 0: the row exists; its code offset is computed per step
   }
   uint32_t xoff[XPER];
   bool xlive[XPER];
@@ -374,9 +376,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_large32_kernel(
       for (int p = 0; p < 2; ++p) {
         wr.s[i][p] = ld16(rs_sm, voff_s[i], b * 1024 + p * 512);
         if (EXPM)
-          wr.e[i][p] = ld16(rs_codes, voff_n[i], b * 1024 + p * 512);
+          wr.e[i][p] = ld16(rs_codes, voff_n[i] | (code_brick_off(b + (uint32_t)pb * kbn, 16, codes_ilv) +
+                                                 code_lane_off(2 * p + ks2, r, 16, codes_ilv)), 0);
         else
-          wr.n[i][p] = ld8(rs_codes, voff_n[i], b * 512 + p * 256);
+          wr.n[i][p] = ld8(rs_codes, voff_n[i] | (code_brick_off(b + (uint32_t)pb * kbn, 8, codes_ilv) +
+                                                code_lane_off(2 * p + ks2, r, 8, codes_ilv)), 0);
       }
       if (!EXPM) {
         const uint32_t mapa = mnext[i][0].x, mapb = mnext[i][1].x;
@@ -494,11 +498,11 @@ hipError_t launch_large32_t(const FusedW& w, const uint16_t* x, float* y, int64_
   if (w.exp_mode)
     hipLaunchKernelGGL((fused_large32_kernel<WAVES, RB2, TB2, true>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                        w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
-                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   else
     hipLaunchKernelGGL((fused_large32_kernel<WAVES, RB2, TB2, false>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                        w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
-                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.rows, (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 
@@ -525,7 +529,7 @@ __global__ __launch_bounds__(256) void fused_large_il_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    int ksplit, int n_tblk, int n_rblk) {
+    int ksplit, int n_tblk, int n_rblk, uint64_t codes_bytes, int codes_ilv) {
   constexpr int WAVES = 4, RB2 = 2, TB2 = 8;
   constexpr int TOK = 32 * TB2;
   constexpr int XPER = TOK * 8 / (WAVES * 64);
@@ -557,7 +561,7 @@ __global__ __launch_bounds__(256) void fused_large_il_kernel(
   const uint32_t lut[4] = {in_vgpr(lut0), in_vgpr(lut1), in_vgpr(lut2), in_vgpr(lut3)};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
-  const rsrc_t rs_codes = make_rsrc(codes, EXPM ? nweights : nweights / 2);
+  const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
   const uint32_t run = (uint32_t)(ks2 * 16 + r);
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(256) void fused_large_il_kernel(
   for (int rb = 0; rb < RB2; ++rb) {
     const bool ok = brow0 + 2 * rb + pb < brows;
     voff_s[rb] = ok ? run * 16 + (uint32_t)pb * kbn * 1024 : kOffRange;
-    voff_n[rb] = ok ? run * (EXPM ? 16 : 8) + (uint32_t)pb * kbn * (EXPM ? 1024 : 512) : kOffRange;
+    voff_n[rb] = ok ? 0u : kOffRange;  // 0: the row exists; its code offset is computed per step
   }
   uint32_t xoff[XPER];
 #pragma unroll
@@ -604,9 +608,11 @@ __global__ __launch_bounds__(256) void fused_large_il_kernel(
       for (int p = 0; p < 2; ++p) {
         wr.s[i][p] = ld16(rs_sm, voff_s[i], b * 1024 + p * 512);
         if (EXPM)
-          wr.e[i][p] = ld16(rs_codes, voff_n[i], b * 1024 + p * 512);
+          wr.e[i][p] = ld16(rs_codes, voff_n[i] | (code_brick_off(b + (uint32_t)pb * kbn, 16, codes_ilv) +
+                                                 code_lane_off(2 * p + ks2, r, 16, codes_ilv)), 0);
         else
-          wr.n[i][p] = ld8(rs_codes, voff_n[i], b * 512 + p * 256);
+          wr.n[i][p] = ld8(rs_codes, voff_n[i] | (code_brick_off(b + (uint32_t)pb * kbn, 8, codes_ilv) +
+                                                code_lane_off(2 * p + ks2, r, 8, codes_ilv)), 0);
       }
       if (!EXPM) {
         uint2 ma = uint2{0u, 0u}, mb = uint2{0u, 0u};
@@ -822,11 +828,11 @@ hipError_t launch_large_il(const FusedW& w, const uint16_t* x, float* y, int64_t
   if (w.exp_mode)
     hipLaunchKernelGGL((fused_large_il_kernel<true, GROUPED>), grid, dim3(256), 0, s, w.sm, w.codes, w.meta, w.side,
                        w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens, (int)w.rows,
-                       (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   else
     hipLaunchKernelGGL((fused_large_il_kernel<false, GROUPED>), grid, dim3(256), 0, s, w.sm, w.codes, w.meta, w.side,
                        w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens, (int)w.rows,
-                       (int)w.cols, ksplit, n_tblk, n_rblk);
+                       (int)w.cols, ksplit, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    int ksplit) {
+    int ksplit, uint64_t codes_bytes, int codes_ilv) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;  // row inside the brick (A operand row) / token inside a block (B column)
@@ -51,57 +51,62 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   constexpr int STEP = WAVES * U;
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
-  const rsrc_t rs_codes = make_rsrc(codes, EXPM ? nweights : nweights / 2);
+  const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
   // per-lane byte offsets, fixed for the whole kernel
-  const uint32_t lane16 = lane * 16, lane8 = lane * 8;
-  // Lanes of tokens past the batch read at an offset past every buffer's
-  // range: a buffer load there returns zeros and touches no memory.  Every
-  // load is then issued unconditionally, so the compiler can count the loads
-  // in flight and wait for one stage only, not for all of them.
+  const uint32_t lane16 = lane * 16;
+  constexpr uint32_t CS = EXPM ? 16 : 8;  // code-stream bytes per run
+  const uint32_t clane = code_lane_off(q, r, CS, codes_ilv);
   uint32_t xlane[TB];
+  bool xlive[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     const int tok = t * 16 + r;
-    xlane[t] = tok < tokens ? ((uint32_t)tok * cols + q * 16) * 2 : kOffRange;
+    xlive[t] = tok < tokens;
+    xlane[t] = ((uint32_t)tok * cols + q * 16) * 2;
   }
 
   f32x4 acc[TB];
 #pragma unroll
   for (int t = 0; t < TB; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // per-brick table of the stage that will be fetched next (scalar loads)
+  // per-brick table of the stage that will be fetched next
   uint2 mnext[U];
   auto load_meta = [&](int kb0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = min(kb0 + u * WAVES, hi - 1);
-      mnext[u] = EXPM ? uint2{0u, 0u} : meta[brick_row0 + kb];
+      const int kb = kb0 + u * WAVES;
+      mnext[u] = (!EXPM && kb < hi) ? meta[brick_row0 + kb] : uint2{0u, 0u};
     }
   };
-  // A stage past the slice's end re-reads its last brick (the compute step
-  // skips it), which keeps the number of loads per stage fixed.
   auto fetch = [&](Stage<U, TB, EXPM>& st, int kb0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int kb = min(kb0 + u * WAVES, hi - 1);
+      const int kb = kb0 + u * WAVES;
+      if (kb >= hi) break;
       const uint32_t b = (uint32_t)brick_row0 + kb;
       st.s[u] = ld16(rs_sm, lane16, b * 1024);
       if (EXPM) {
-        st.e[u] = ld16(rs_codes, lane16, b * 1024);
+        st.e[u] = ld16(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
       } else {
-        st.n[u] = ld8(rs_codes, lane8, b * 512);
+        st.n[u] = ld8(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
         const uint32_t map = mnext[u].x;
         st.anyraw[u] = map;
         st.raw[u] = (map >> r) & 1u;
-        const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-        st.e[u] = ld16(rs_side, st.raw[u] ? (mnext[u].y + rank) * 64 + q * 16 : kOffRange, 0);
+        if (map && st.raw[u]) {
+          const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
+          st.e[u] = ld16(rs_side, (mnext[u].y + rank) * 64 + q * 16, 0);
+        }
       }
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
-        st.x[u][t][0] = ld16(rs_x, xlane[t], kb * 128);
-        st.x[u][t][1] = ld16(rs_x, xlane[t] + 16, kb * 128);
+        st.x[u][t][0] = u32x4{0u, 0u, 0u, 0u};
+        st.x[u][t][1] = u32x4{0u, 0u, 0u, 0u};
+        if (xlive[t]) {
+          st.x[u][t][0] = ld16(rs_x, xlane[t], kb * 128);
+          st.x[u][t][1] = ld16(rs_x, xlane[t] + 16, kb * 128);
+        }
       }
     }
   };
@@ -141,12 +146,12 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
   fetch(sa, kb);
   load_meta(kb + STEP);
   while (kb < hi) {
-    fetch(sb, kb + STEP);
+    if (kb + STEP < hi) fetch(sb, kb + STEP);
     load_meta(kb + 2 * STEP);
     compute(sa, kb);
     kb += STEP;
     if (kb >= hi) break;
-    fetch(sa, kb + STEP);
+    if (kb + STEP < hi) fetch(sa, kb + STEP);
     load_meta(kb + 2 * STEP);
     compute(sb, kb);
     kb += STEP;
@@ -200,7 +205,8 @@ template <int WAVES, int D>
 __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
-    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols) {
+    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
+    uint64_t codes_bytes, int codes_ilv) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -209,10 +215,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
   const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
-  const rsrc_t rs_codes = make_rsrc(codes, nweights / 2);
+  const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
-  const uint32_t lane16 = lane * 16, lane8 = lane * 8;
+  const uint32_t lane16 = lane * 16;
+  const uint32_t clane = code_lane_off(q, r, 8, codes_ilv);
   const bool live = r < tokens;
   // LDS: x (tokens x cols bf16), a 32-byte zero tail read by lanes of absent
   // tokens, then the brick-row's per-brick table
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     const uint32_t before = __builtin_amdgcn_readfirstlane(m.y);
     const uint32_t b = brick_row0 + kb;
     st.s = ld16(rs_sm, lane16, b * 1024);
-    st.n = ld8(rs_codes, lane8, b * 512);
+    st.n = ld8(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
     st.map = map;
     const bool raw = (map >> r) & 1u;
     const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
@@ -321,7 +328,7 @@ hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tok
   const size_t lds = (size_t)tokens * w.cols * 2 + 32 + (size_t)(w.cols / 64) * 8;
   hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s, w.sm,
                      w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
-                     (int)tokens, (int)w.rows, (int)w.cols);
+                     (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 
@@ -330,7 +337,7 @@ hipError_t launch_one(const FusedW& w, const uint16_t* x, float* y, int64_t toke
   dim3 grid((unsigned)(w.rows / 16), (unsigned)ksplit);
   hipLaunchKernelGGL((fused_small_kernel<WAVES, TB, EXPM, U>), grid, dim3(WAVES * 64), 0, s, w.sm, w.codes,
                      w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,
-                     (int)w.rows, (int)w.cols, ksplit);
+                     (int)w.rows, (int)w.cols, ksplit, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 

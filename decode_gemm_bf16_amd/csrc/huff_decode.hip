@@ -6,18 +6,25 @@
 // or a transcode to 4-bit palette codes (pipeline 3, a quarter).
 //
 // A lane decodes two chunks of 256 symbols each, from their bit offsets, in
-// lockstep (two independent dependency chains per lane).  The 12-bit code limit makes one 4096-entry table (symbol | length
-// << 8) in LDS decode any code with a single lookup on the top 12 bits of a
-// 64-bit bit buffer.  The 256 chunks of a workgroup are consecutive in the
-// stream, so their bits are first copied into LDS with coalesced 16-byte
-// loads; the bit buffer then refills from LDS, never waiting on HBM inside the
-// symbol loop.  (A workgroup whose span does not fit, which needs more than
-// 4 bits per exponent on average, reads its words from global memory.)
+// lockstep (two independent dependency chains per lane).  Decoding is a chain
+// of dependent table lookups -- the position of a code is known only once the
+// previous one is decoded -- so its time is the chain's length times the LDS
+// round trip.  The 12-bit code limit lets one 4096-entry table in LDS decode,
+// from the top 12 bits of a 64-bit bit buffer, every whole code those bits
+// hold, up to three: with exponent codes of 2-3 bits on average a lookup
+// yields about three symbols, a third of the chain.  Symbols gather in a
+// 64-bit queue per chunk; a run (16 symbols) is emitted once both chains of
+// every lane of the wave hold one.  The 256 chunks of a workgroup are
+// consecutive in the stream, so their bits are first copied into LDS with
+// coalesced 16-byte loads; the bit buffer then refills from LDS, never
+// waiting on HBM inside the symbol loop.  (A workgroup whose span does not
+// fit, which needs about 3 bits per exponent on average, reads its words
+// from global memory.)
 //
 // A chunk is a quarter brick: 16 runs of 16 symbols, run i = row i of the
-// brick, 16 consecutive columns.  All lanes of a wave finish a run in the same
-// step, so a run is emitted by the whole wave at once; for the bf16 output
-// consecutive lanes write consecutive 32-byte pieces of one output row.
+// brick, 16 consecutive columns.  All lanes of a wave emit a run in the same
+// step; for the bf16 output consecutive lanes write consecutive 32-byte
+// pieces of one output row.
 #include "kernels.h"
 #include "recon.h"
 
@@ -26,7 +33,8 @@ namespace {
 
 constexpr int kChunksPerBlock = 256;
 constexpr int kThreads = 128;      // two chunks per lane
-constexpr int kStageWords = 7680;  // 30 KB of staged bitstream: 4 workgroups fit one CU's LDS
+constexpr int kStreamPad = 8;      // zero words after the stream (the encoder's padding)
+constexpr int kStageWords = 6016;  // 23.5 KB of staged bitstream: with the 16 KB table, 4 workgroups per CU
 
 // Bit reader over one chunk: a 64-bit buffer with `nbits` valid bits at the
 // top, the next stream word already fetched, and the index of the one after.
@@ -48,18 +56,23 @@ __device__ __forceinline__ Reader reader_at(Src src, uint32_t base, uint32_t sta
   return rd;
 }
 
-// Decode one symbol: a single lookup on the top 12 bits.
-__device__ __forceinline__ uint32_t take(Reader& rd, const uint16_t* lut) {
+// Symbols decoded but not yet placed in a run, first in the low byte.
+struct Queue {
+  uint64_t q;
+  int n;
+};
+
+// One lookup on the top 12 bits: append its symbols (1 to 3) to the queue and
+// keep at least 32 valid bits in the buffer (a lookup takes at most 12).
+template <class Src>
+__device__ __forceinline__ void take(Reader& rd, Queue& qu, const uint32_t* lut, Src src) {
   const uint32_t ent = lut[(uint32_t)(rd.buf >> 52)];
-  const int len = (int)(ent >> 8);
+  const int cnt = (int)((ent >> 24) & 3u);
+  const int len = (int)(ent >> 26);
+  qu.q |= (uint64_t)(ent & 0xFFFFFFu) << (8 * qu.n);
+  qu.n += cnt;
   rd.buf <<= len;
   rd.nbits -= len;
-  return ent & 0xFFu;
-}
-
-// After two symbols (at most 24 bits) keep at least 32 valid bits.
-template <class Src>
-__device__ __forceinline__ void refill(Reader& rd, Src src) {
   if (rd.nbits < 32) {
     rd.buf |= (uint64_t)rd.next << (32 - rd.nbits);
     rd.nbits += 32;
@@ -67,13 +80,28 @@ __device__ __forceinline__ void refill(Reader& rd, Src src) {
   }
 }
 
+// Move four queued symbols into dword `k` of the run being built.
+__device__ __forceinline__ void put(Queue& qu, uint32_t e[4], int& k) {
+  const uint32_t d = (uint32_t)qu.q;
+  e[0] = k == 0 ? d : e[0];
+  e[1] = k == 1 ? d : e[1];
+  e[2] = k == 2 ? d : e[2];
+  e[3] = k == 3 ? d : e[3];
+  qu.q >>= 32;
+  qu.n -= 4;
+  ++k;
+}
+
 template <int EMIT>
 __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int run, const uint8_t* code_of,
-                                         const uint8_t* __restrict__ sm, uint32_t rawmap, void* __restrict__ out,
-                                         int cols) {
-  const int64_t serial = c * 256 + run * 16;
+                                         const u32x4& s, uint32_t rawmap, void* __restrict__ out, int cols) {
+  // exponent bytes and 4-bit codes go to the interleaved scratch order (runs
+  // of 64 consecutive chunks side by side, see code_lane_off in recon.h): the
+  // 64 lanes of a wave, 64 consecutive chunks, store one run as one
+  // contiguous block instead of 64 pieces 256 bytes apart
+  const int64_t ilv_run = ((c >> 6) * 16 + run) * 64 + (c & 63);
   if (EMIT == EMIT_EXP) {
-    *(u32x4*)((uint8_t*)out + serial) = u32x4{ew[0], ew[1], ew[2], ew[3]};
+    *(u32x4*)((uint8_t*)out + ilv_run * 16) = u32x4{ew[0], ew[1], ew[2], ew[3]};
   } else if (EMIT == EMIT_NIBBLE) {
     uint32_t nw0 = 0u, nw1 = 0u;
     if (!((rawmap >> run) & 1u)) {
@@ -85,9 +113,8 @@ __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int ru
         if (j < 8) nw0 |= code << shift; else nw1 |= code << shift;
       }
     }
-    *(u32x2*)((uint8_t*)out + serial / 2) = u32x2{nw0, nw1};
+    *(u32x2*)((uint8_t*)out + ilv_run * 8) = u32x2{nw0, nw1};
   } else {
-    const u32x4 s = *(const u32x4*)(sm + serial);
     uint32_t p[8];
     rebuild_exp(s, u32x4{ew[0], ew[1], ew[2], ew[3]}, p);
     const int kbn = cols >> 6;
@@ -99,47 +126,57 @@ __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int ru
 }
 
 // Two chunks per lane, decoded in lockstep: their lookups are independent, so
-// one chain's LDS latency hides behind the other's.
+// one chain's LDS latency hides behind the other's.  Per run, each chain takes
+// a lookup while its queue holds fewer than 4 symbols and moves 4 symbols into
+// the run whenever it holds them; a run needs at most 16 lookups (a lookup
+// yields at least one symbol), which bounds the loop.
 template <int EMIT, class Src>
 __device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
-                                           const uint32_t* __restrict__ offsets, const uint16_t* lut,
+                                           const uint32_t* __restrict__ offsets, const uint32_t* lut,
                                            const uint8_t* code_of, const uint8_t* __restrict__ sm,
                                            const uint2* __restrict__ meta, void* __restrict__ out, int cols) {
   Reader ra = reader_at(src, base, offsets[ca]);
   Reader rb = has_b ? reader_at(src, base, offsets[cb]) : ra;
   const uint32_t rawa = EMIT == EMIT_NIBBLE ? meta[ca >> 2].x : 0u;
   const uint32_t rawb = (EMIT == EMIT_NIBBLE && has_b) ? meta[cb >> 2].x : 0u;
+  Queue qa = {0ull, 0}, qb = {0ull, 0};
+  // bf16 output: the run's sign+mantissa bytes, requested one run ahead
+  u32x4 sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u}, na = sa, nb = sb;
+  if (EMIT == EMIT_BF16) {
+    na = *(const u32x4*)(sm + ca * 256);
+    if (has_b) nb = *(const u32x4*)(sm + cb * 256);
+  }
   for (int run = 0; run < 16; ++run) {
-    uint32_t ea[4] = {0u, 0u, 0u, 0u}, eb[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      ea[j >> 2] |= take(ra, lut) << (8 * (j & 3));
-      eb[j >> 2] |= take(rb, lut) << (8 * (j & 3));
-      if (j & 1) {
-        refill(ra, src);
-        refill(rb, src);
+    if (EMIT == EMIT_BF16) {
+      sa = na;
+      sb = nb;
+      if (run + 1 < 16) {
+        na = *(const u32x4*)(sm + ca * 256 + (run + 1) * 16);
+        if (has_b) nb = *(const u32x4*)(sm + cb * 256 + (run + 1) * 16);
       }
     }
-    emit_run<EMIT>(ea, ca, run, code_of, sm, rawa, out, cols);
-    if (has_b) emit_run<EMIT>(eb, cb, run, code_of, sm, rawb, out, cols);
+    uint32_t ea[4] = {0u, 0u, 0u, 0u}, eb[4] = {0u, 0u, 0u, 0u};
+    int ka = 0, kb = 0;
+    for (int it = 0; it < 16; ++it) {
+      if (qa.n < 4) take(ra, qa, lut, src);
+      if (qb.n < 4) take(rb, qb, lut, src);
+      if (ka < 4 && qa.n >= 4) put(qa, ea, ka);
+      if (kb < 4 && qb.n >= 4) put(qb, eb, kb);
+      if (!__any(ka < 4 || kb < 4)) break;  // every run of the wave is complete
+    }
+    emit_run<EMIT>(ea, ca, run, code_of, sa, rawa, out, cols);
+    if (has_b) emit_run<EMIT>(eb, cb, run, code_of, sb, rawb, out, cols);
   }
 }
 
 template <int EMIT>
 __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
     const uint32_t* __restrict__ words, uint64_t total_bits, const uint32_t* __restrict__ offsets,
-    const uint16_t* __restrict__ lut_g, const uint8_t* __restrict__ sm, const uint2* __restrict__ meta,
+    const uint32_t* __restrict__ lut_g, const uint8_t* __restrict__ sm, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ code_of_g, void* __restrict__ out, int64_t nchunks, int cols) {
-  __shared__ uint16_t lut[4096];
+  __shared__ uint32_t lut[4096];
   __shared__ uint8_t code_of[256];
   __shared__ uint32_t stage[kStageWords];
-  {
-    const u32x4* src = (const u32x4*)lut_g;
-    u32x4* dst = (u32x4*)lut;
-    for (int i = threadIdx.x; i < 4096 * 2 / 16; i += kThreads) dst[i] = src[i];
-    if (EMIT == EMIT_NIBBLE)
-      for (int i = threadIdx.x; i < 256; i += kThreads) code_of[i] = code_of_g[i];
-  }
   const int64_t c0 = (int64_t)blockIdx.x * kChunksPerBlock;
   const int64_t c_end = c0 + kChunksPerBlock < nchunks ? c0 + kChunksPerBlock : nchunks;
   // words that the chunks c0 .. c_end-1 read: from the first chunk's start to
@@ -148,17 +185,38 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   const uint64_t end_bit = c_end < nchunks ? (uint64_t)offsets[c_end] : total_bits;
   const uint32_t w1 = (uint32_t)(end_bit >> 5) + 4;
   const bool staged = w1 - w0 <= (uint32_t)kStageWords;
-  if (staged) {
-    // 16-byte aligned copy of words [w0 & ~3, w1), clipped to the stage
+  {
+    // The decode table, the palette codes and the 16-byte aligned span of
+    // words [w0 & ~3, w1) go to LDS: every load is issued before the first
+    // store, so the copy costs one memory latency, not one per iteration.
+    constexpr int LV = 4096 * 4 / 16 / kThreads;             // table pieces per thread
+    constexpr int SV = (kStageWords / 4 + 2 + kThreads - 1) / kThreads;  // stream pieces per thread
+    const rsrc_t rs_lut = make_rsrc(lut_g, 4096 * 4);
+    const rsrc_t rs_words = make_rsrc(words, (((total_bits + 31) >> 5) + kStreamPad) * 4);
+    const rsrc_t rs_code = make_rsrc(code_of_g, 256);
     const uint32_t a0 = w0 & ~3u;
-    const uint32_t nvec = (w1 - a0 + 3) / 4;
-    for (uint32_t i = threadIdx.x; i < nvec; i += kThreads) {
-      const uint32_t wv = a0 + 4 * i;
-      const u32x4 v = *(const u32x4*)(words + wv);
+    const uint32_t nvec = staged ? (w1 - a0 + 3) / 4 : 0u;
+    u32x4 lv[LV], sv[SV], cv;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int32_t d = (int32_t)(wv + k) - (int32_t)w0;
-        if (d >= 0 && d < kStageWords) stage[d] = v[k];
+    for (int k = 0; k < LV; ++k) lv[k] = ld16(rs_lut, (threadIdx.x + k * kThreads) * 16, 0);
+#pragma unroll
+    for (int k = 0; k < SV; ++k) {
+      const uint32_t i = threadIdx.x + k * kThreads;
+      sv[k] = ld16(rs_words, i < nvec ? (a0 + 4 * i) * 4 : kOffRange, 0);
+    }
+    cv = ld16(rs_code, EMIT == EMIT_NIBBLE && threadIdx.x < 16 ? threadIdx.x * 16 : kOffRange, 0);
+#pragma unroll
+    for (int k = 0; k < LV; ++k) ((u32x4*)lut)[threadIdx.x + k * kThreads] = lv[k];
+    if (EMIT == EMIT_NIBBLE && threadIdx.x < 16) ((u32x4*)code_of)[threadIdx.x] = cv;
+#pragma unroll
+    for (int k = 0; k < SV; ++k) {
+      const uint32_t i = threadIdx.x + k * kThreads;
+      if (i < nvec) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int32_t d = (int32_t)(a0 + 4 * i + kk) - (int32_t)w0;
+          if (d >= 0 && d < kStageWords) stage[d] = sv[k][kk];
+        }
       }
     }
   }

@@ -17,6 +17,8 @@ struct FusedW {
   uint32_t lut[4];         // palette mode: entry i = rotr8(palette[i], 1) at byte i%4 of lut[i/4]
   int64_t rows, cols;
   bool exp_mode;           // codes are exponent bytes (pipeline 2)
+  bool codes_ilv;          // codes are in the interleaved scratch order (pipelines 2, 3; see recon.h)
+  uint64_t codes_bytes;    // size of the codes buffer
 };
 
 // Fused-kernel variants.  Small-batch kernels (tokens <= 64): one workgroup per
@@ -52,7 +54,7 @@ enum DecodeEmit { EMIT_BF16 = 0, EMIT_EXP = 1, EMIT_NIBBLE = 2 };
 struct HuffDev {
   const uint32_t* words;
   const uint32_t* offsets;
-  const uint16_t* lut;      // 4096 entries: symbol | length << 8
+  const uint32_t* lut;      // 4096 entries: up to 3 symbols | count << 24 | bits << 26
   const uint8_t* sm;        // EMIT_BF16
   const uint2* meta;        // EMIT_NIBBLE: per-brick raw map
   const uint8_t* code_of;   // EMIT_NIBBLE: 256 entries, code of each palette exponent

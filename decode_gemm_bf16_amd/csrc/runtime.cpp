@@ -142,7 +142,7 @@ struct uw_matrix {
   uint8_t* d_code_of = nullptr;
   uint32_t* d_words = nullptr;
   uint32_t* d_offsets = nullptr;
-  uint16_t* d_lut = nullptr;
+  uint32_t* d_lut = nullptr;  // multi-symbol decode table (4096 entries)
   uint32_t lut_v[4] = {};
   uint64_t words_total = 0;  // payload + padding words on the device
   hipStream_t main = nullptr, side = nullptr;
@@ -158,11 +158,13 @@ struct uw_matrix {
   bool has(uint32_t f) const { return (formats & f) != 0; }
   bool has_pal_tables() const { return has(UW_FMT_PALETTE) || has(UW_FMT_RAWAUX); }
   size_t scratch_need(int p) const {
-    const size_t n = size_t(rows) * size_t(cols);
+    // pipelines 2 and 3: the interleaved order pads to whole groups of 64
+    // chunks (64 x 256 weights)
+    const size_t n = size_t(rows) * size_t(cols), groups = (n / 256 + 63) / 64;
     switch (p) {
       case 1: return align256(2 * n);
-      case 2: return align256(n);
-      case 3: return align256(n / 2);
+      case 2: return groups * 64 * 256;
+      case 3: return groups * 64 * 128;
       default: return 0;
     }
   }
@@ -170,10 +172,14 @@ struct uw_matrix {
 
 namespace {
 
+// codes: the resident 4-bit codes (serial order) or the pipeline 2/3 scratch
+// (interleaved order, written by the Huffman decoder)
 uw::FusedW fused_view(const uw_matrix* h, bool exp_mode, const uint8_t* codes) {
   uw::FusedW f;
   f.sm = h->d_sm;
   f.codes = codes;
+  f.codes_ilv = codes != h->d_nib;
+  f.codes_bytes = f.codes_ilv ? h->scratch_need(exp_mode ? 2 : 3) : size_t(h->rows) * size_t(h->cols) / 2;
   f.meta = h->d_meta;
   f.side = h->d_side;
   f.side_bytes = std::max<uint64_t>(h->hf.n_raw * 64, 64);
@@ -325,7 +331,7 @@ uw_status upload(uw_matrix* h) {
   const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
   if (pal) total += align256(n / 2);
   if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64)) + align256(256);
-  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + align256(uw::kLutSize * 2);
+  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + align256(uw::kLutSize * 4);
   if (hipMalloc(&h->dmem, total) != hipSuccess) {
     h->dmem = nullptr;
     return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", total);
@@ -361,8 +367,9 @@ uw_status upload(uw_matrix* h) {
     UW_HIP(hipMemcpy(h->d_words, f.words.data(), f.words.size() * 4, hipMemcpyHostToDevice));
     h->d_offsets = carve<uint32_t>(cur, f.offsets.size() * 4);
     UW_HIP(hipMemcpy(h->d_offsets, f.offsets.data(), f.offsets.size() * 4, hipMemcpyHostToDevice));
-    h->d_lut = carve<uint16_t>(cur, uw::kLutSize * 2);
-    UW_HIP(hipMemcpy(h->d_lut, f.lut.data(), uw::kLutSize * 2, hipMemcpyHostToDevice));
+    const std::vector<uint32_t> lut3 = uw::multi_symbol_table(f.lut);
+    h->d_lut = carve<uint32_t>(cur, uw::kLutSize * 4);
+    UW_HIP(hipMemcpy(h->d_lut, lut3.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
     h->words_total = f.words.size();
   }
   if (tabs) {
