@@ -207,7 +207,8 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
     }
     uint64_t total = 0;
     for (int s = 0; s < 256; ++s) total += f.hist[s] * f.lengths[s];
-    if (total >= (uint64_t(1) << 32)) return "Huffman stream longer than 2^32 bits";
+    // bit positions are 32-bit on the device, look-ahead past the last code included
+    if (total >= (uint64_t(1) << 32) - 1024) return "Huffman stream longer than 2^32 - 1024 bits";
     f.stream_bits = total;
     const uint64_t payload = (total + 31) / 32;
     f.words.assign(payload + kStreamPadWords, 0);

@@ -10,16 +10,18 @@
 // of dependent table lookups -- the position of a code is known only once the
 // previous one is decoded -- so its time is the chain's length times the LDS
 // round trip.  The 12-bit code limit lets one 4096-entry table in LDS decode,
-// from the top 12 bits of a 64-bit bit buffer, every whole code those bits
+// from the 12 bits at the chain's bit position, every whole code those bits
 // hold, up to three: with exponent codes of 2-3 bits on average a lookup
-// yields about three symbols, a third of the chain.  Symbols gather in a
-// 64-bit queue per chunk; a run (16 symbols) is emitted once both chains of
-// every lane of the wave hold one.  The 256 chunks of a workgroup are
-// consecutive in the stream, so their bits are first copied into LDS with
-// coalesced 16-byte loads; the bit buffer then refills from LDS, never
-// waiting on HBM inside the symbol loop.  (A workgroup whose span does not
-// fit, which needs about 3 bits per exponent on average, reads its words
-// from global memory.)
+// yields about three symbols, a third of the chain.  A step reads the two
+// stream words around the position (one LDS instruction) and shifts out a
+// 32-bit window -- no bit buffer to refill -- and every step is branch-free,
+// so a wave whose lanes are at different points of their runs runs one
+// instruction stream.  Symbols gather in a 64-bit queue per chunk; a run (16
+// symbols) is emitted once both chains of every lane of the wave hold one.
+// The 256 chunks of a workgroup are consecutive in the stream, so their bits
+// are first copied into LDS with coalesced 16-byte loads.  (A workgroup whose
+// span does not fit, which needs about 3 bits per exponent on average, reads
+// its words from global memory.)
 //
 // A chunk is a quarter brick: 16 runs of 16 symbols, run i = row i of the
 // brick, 16 consecutive columns.  All lanes of a wave emit a run in the same
@@ -36,24 +38,13 @@ constexpr int kThreads = 128;      // two chunks per lane
 constexpr int kStreamPad = 8;      // zero words after the stream (the encoder's padding)
 constexpr int kStageWords = 6016;  // 23.5 KB of staged bitstream: with the 16 KB table, 4 workgroups per CU
 
-// Bit reader over one chunk: a 64-bit buffer with `nbits` valid bits at the
-// top, the next stream word already fetched, and the index of the one after.
-struct Reader {
-  uint64_t buf;
-  int nbits;
-  uint32_t next;
-  uint32_t wi;
-};
-
+// The next 32 bits of the stream from bit `pos` (MSB first): two consecutive
+// words and a 64-bit shift.
 template <class Src>
-__device__ __forceinline__ Reader reader_at(Src src, uint32_t base, uint32_t start) {
-  Reader rd;
-  uint32_t wi = (start >> 5) - base;
-  rd.buf = (((uint64_t)src(wi) << 32) | src(wi + 1)) << (start & 31);
-  rd.nbits = 64 - (int)(start & 31);  // >= 33
-  rd.next = src(wi + 2);
-  rd.wi = wi + 3;
-  return rd;
+__device__ __forceinline__ uint32_t window(Src src, uint32_t pos) {
+  const uint32_t wi = pos >> 5;
+  const uint64_t two = ((uint64_t)src(wi) << 32) | src(wi + 1);
+  return (uint32_t)((two << (pos & 31)) >> 32);
 }
 
 // Symbols decoded but not yet placed in a run, first in the low byte.
@@ -62,34 +53,27 @@ struct Queue {
   int n;
 };
 
-// One lookup on the top 12 bits: append its symbols (1 to 3) to the queue and
-// keep at least 32 valid bits in the buffer (a lookup takes at most 12).
+// One chain step, branch-free: a lookup on the 12 bits at `pos` whose symbols
+// (1 to 3) join the queue when the queue holds fewer than 4 (else the entry
+// is dropped and nothing moves), then 4 queued symbols move into the run being
+// built when it is not complete -- the run's dwords shift down one place and
+// the new one enters last, so after four moves they are in order.
 template <class Src>
-__device__ __forceinline__ void take(Reader& rd, Queue& qu, const uint32_t* lut, Src src) {
-  const uint32_t ent = lut[(uint32_t)(rd.buf >> 52)];
-  const int cnt = (int)((ent >> 24) & 3u);
-  const int len = (int)(ent >> 26);
+__device__ __forceinline__ void step(Src src, uint32_t& pos, Queue& qu, uint32_t e[4], int& k,
+                                     const uint32_t* lut) {
+  uint32_t ent = lut[window(src, pos) >> 20];
+  ent = qu.n < 4 ? ent : 0u;
+  pos += ent >> 26;
   qu.q |= (uint64_t)(ent & 0xFFFFFFu) << (8 * qu.n);
-  qu.n += cnt;
-  rd.buf <<= len;
-  rd.nbits -= len;
-  if (rd.nbits < 32) {
-    rd.buf |= (uint64_t)rd.next << (32 - rd.nbits);
-    rd.nbits += 32;
-    rd.next = src(rd.wi++);
-  }
-}
-
-// Move four queued symbols into dword `k` of the run being built.
-__device__ __forceinline__ void put(Queue& qu, uint32_t e[4], int& k) {
-  const uint32_t d = (uint32_t)qu.q;
-  e[0] = k == 0 ? d : e[0];
-  e[1] = k == 1 ? d : e[1];
-  e[2] = k == 2 ? d : e[2];
-  e[3] = k == 3 ? d : e[3];
-  qu.q >>= 32;
-  qu.n -= 4;
-  ++k;
+  qu.n += (int)((ent >> 24) & 3u);
+  const bool mv = qu.n >= 4 && k < 4;
+  e[0] = mv ? e[1] : e[0];
+  e[1] = mv ? e[2] : e[1];
+  e[2] = mv ? e[3] : e[2];
+  e[3] = mv ? (uint32_t)qu.q : e[3];
+  qu.q = mv ? qu.q >> 32 : qu.q;
+  qu.n -= mv ? 4 : 0;
+  k += mv ? 1 : 0;
 }
 
 template <int EMIT>
@@ -126,17 +110,16 @@ __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int ru
 }
 
 // Two chunks per lane, decoded in lockstep: their lookups are independent, so
-// one chain's LDS latency hides behind the other's.  Per run, each chain takes
-// a lookup while its queue holds fewer than 4 symbols and moves 4 symbols into
-// the run whenever it holds them; a run needs at most 16 lookups (a lookup
-// yields at least one symbol), which bounds the loop.
+// one chain's LDS latency hides behind the other's.  A run needs at most 16
+// steps (each step's lookup yields at least one symbol), which bounds the
+// loop; the wave leaves it as soon as every run of the wave is complete.
 template <int EMIT, class Src>
 __device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
                                            const uint32_t* __restrict__ offsets, const uint32_t* lut,
                                            const uint8_t* code_of, const uint8_t* __restrict__ sm,
                                            const uint2* __restrict__ meta, void* __restrict__ out, int cols) {
-  Reader ra = reader_at(src, base, offsets[ca]);
-  Reader rb = has_b ? reader_at(src, base, offsets[cb]) : ra;
+  uint32_t pa = offsets[ca] - base * 32;
+  uint32_t pb = has_b ? offsets[cb] - base * 32 : pa;
   const uint32_t rawa = EMIT == EMIT_NIBBLE ? meta[ca >> 2].x : 0u;
   const uint32_t rawb = (EMIT == EMIT_NIBBLE && has_b) ? meta[cb >> 2].x : 0u;
   Queue qa = {0ull, 0}, qb = {0ull, 0};
@@ -158,10 +141,8 @@ __device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, i
     uint32_t ea[4] = {0u, 0u, 0u, 0u}, eb[4] = {0u, 0u, 0u, 0u};
     int ka = 0, kb = 0;
     for (int it = 0; it < 16; ++it) {
-      if (qa.n < 4) take(ra, qa, lut, src);
-      if (qb.n < 4) take(rb, qb, lut, src);
-      if (ka < 4 && qa.n >= 4) put(qa, ea, ka);
-      if (kb < 4 && qb.n >= 4) put(qb, eb, kb);
+      step(src, pa, qa, ea, ka, lut);
+      step(src, pb, qb, eb, kb, lut);
       if (!__any(ka < 4 || kb < 4)) break;  // every run of the wave is complete
     }
     emit_run<EMIT>(ea, ca, run, code_of, sa, rawa, out, cols);
