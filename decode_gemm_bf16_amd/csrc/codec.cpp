@@ -260,4 +260,15 @@ std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut) {
   return out;
 }
 
+std::vector<uint32_t> multi_code_table(const std::vector<uint32_t>& multi, const uint8_t code_of[256]) {
+  std::vector<uint32_t> out(multi.size());
+  for (size_t p = 0; p < multi.size(); ++p) {
+    const uint32_t e = multi[p], cnt = (e >> 24) & 3u;
+    uint32_t codes = 0;
+    for (uint32_t i = 0; i < cnt; ++i) codes |= uint32_t(code_of[(e >> (8 * i)) & 0xFFu] & 0xFu) << (4 * i);
+    out[p] = codes | (e & 0xFF000000u);
+  }
+  return out;
+}
+
 }  // namespace uw

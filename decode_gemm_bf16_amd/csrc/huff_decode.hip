@@ -18,6 +18,8 @@
 // so a wave whose lanes are at different points of their runs runs one
 // instruction stream.  Symbols gather in a 64-bit queue per chunk; a run (16
 // symbols) is emitted once both chains of every lane of the wave hold one.
+// Pipeline 3 uses a second table whose entries hold the symbols' 4-bit palette
+// codes, so the transcode is a nibble shuffle per 8 codes.
 // The 256 chunks of a workgroup are consecutive in the stream, so their bits
 // are first copied into LDS with coalesced 16-byte loads.  (A workgroup whose
 // span does not fit, which needs about 3 bits per exponent on average, reads
@@ -47,38 +49,48 @@ __device__ __forceinline__ uint32_t window(Src src, uint32_t pos) {
   return (uint32_t)((two << (pos & 31)) >> 32);
 }
 
-// Symbols decoded but not yet placed in a run, first in the low byte.
+// Symbols (or 4-bit codes) decoded but not yet placed in a run, first in the
+// low bits.
 struct Queue {
   uint64_t q;
   int n;
 };
 
-// One chain step, branch-free: a lookup on the 12 bits at `pos` whose symbols
-// (1 to 3) join the queue when the queue holds fewer than 4 (else the entry
-// is dropped and nothing moves), then 4 queued symbols move into the run being
-// built when it is not complete -- the run's dwords shift down one place and
-// the new one enters last, so after four moves they are in order.
-template <class Src>
-__device__ __forceinline__ void step(Src src, uint32_t& pos, Queue& qu, uint32_t e[4], int& k,
-                                     const uint32_t* lut) {
+// One chain step, branch-free.  BITS = 8: the table yields exponent symbols;
+// BITS = 4: it yields their palette codes (pipeline 3).  A lookup on the 12
+// bits at `pos` appends its 1 to 3 entries to the queue when the queue holds
+// less than a dword (else the entry is dropped and nothing moves); then a
+// dword of queued entries moves into the run being built when the run is not
+// complete -- the run's dwords shift down one place and the new one enters
+// last, so they end in order.
+template <int BITS, class Src>
+__device__ __forceinline__ void step(Src src, uint32_t& pos, Queue& qu, uint32_t* e, int& k, const uint32_t* lut) {
+  constexpr int PER = 32 / BITS;       // entries per dword
+  constexpr int RD = 16 * BITS / 32;   // dwords per run
+  constexpr uint32_t MASK = BITS == 8 ? 0xFFFFFFu : 0xFFFu;
   uint32_t ent = lut[window(src, pos) >> 20];
-  ent = qu.n < 4 ? ent : 0u;
+  ent = qu.n < PER ? ent : 0u;
   pos += ent >> 26;
-  qu.q |= (uint64_t)(ent & 0xFFFFFFu) << (8 * qu.n);
+  qu.q |= (uint64_t)(ent & MASK) << (BITS * qu.n);
   qu.n += (int)((ent >> 24) & 3u);
-  const bool mv = qu.n >= 4 && k < 4;
-  e[0] = mv ? e[1] : e[0];
-  e[1] = mv ? e[2] : e[1];
-  e[2] = mv ? e[3] : e[2];
-  e[3] = mv ? (uint32_t)qu.q : e[3];
+  const bool mv = qu.n >= PER && k < RD;
+  if constexpr (RD == 4) {
+    e[0] = mv ? e[1] : e[0];
+    e[1] = mv ? e[2] : e[1];
+    e[2] = mv ? e[3] : e[2];
+    e[3] = mv ? (uint32_t)qu.q : e[3];
+  } else {
+    e[0] = mv ? e[1] : e[0];
+    e[1] = mv ? (uint32_t)qu.q : e[1];
+  }
   qu.q = mv ? qu.q >> 32 : qu.q;
-  qu.n -= mv ? 4 : 0;
+  qu.n -= mv ? PER : 0;
   k += mv ? 1 : 0;
 }
 
 template <int EMIT>
-__device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int run, const uint8_t* code_of,
-                                         const u32x4& s, uint32_t rawmap, void* __restrict__ out, int cols) {
+__device__ __forceinline__ void emit_run(const uint32_t* ew, int64_t c, int run, const u32x4& s, uint32_t rawmap,
+                                         void* __restrict__ out, int cols) {
   // exponent bytes and 4-bit codes go to the interleaved scratch order (runs
   // of 64 consecutive chunks side by side, see code_lane_off in recon.h): the
   // 64 lanes of a wave, 64 consecutive chunks, store one run as one
@@ -87,17 +99,20 @@ __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int ru
   if (EMIT == EMIT_EXP) {
     *(u32x4*)((uint8_t*)out + ilv_run * 16) = u32x4{ew[0], ew[1], ew[2], ew[3]};
   } else if (EMIT == EMIT_NIBBLE) {
-    uint32_t nw0 = 0u, nw1 = 0u;
+    // ew[0..1]: the run's 16 codes in order, 8 per dword (code i at bits 4i);
+    // stored form: of 8 codes, byte b = code b | code b+4 << 4
+    uint32_t nw[2] = {0u, 0u};
     if (!((rawmap >> run) & 1u)) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t code = code_of[(ew[j >> 2] >> (8 * (j & 3))) & 0xFFu];
-        const int jj = j & 7;
-        const int shift = 8 * (jj & 3) + 4 * (jj >> 2);
-        if (j < 8) nw0 |= code << shift; else nw1 |= code << shift;
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t even = ew[h] & 0x0F0F0F0Fu;         // codes 0,2,4,6
+        const uint32_t odd = (ew[h] >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
+        const uint32_t first = __builtin_amdgcn_perm(odd, even, 0x05010400u);   // codes 0..3
+        const uint32_t second = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // codes 4..7
+        nw[h] = first | (second << 4);
       }
     }
-    *(u32x2*)((uint8_t*)out + ilv_run * 8) = u32x2{nw0, nw1};
+    *(u32x2*)((uint8_t*)out + ilv_run * 8) = u32x2{nw[0], nw[1]};
   } else {
     uint32_t p[8];
     rebuild_exp(s, u32x4{ew[0], ew[1], ew[2], ew[3]}, p);
@@ -116,7 +131,7 @@ __device__ __forceinline__ void emit_run(const uint32_t ew[4], int64_t c, int ru
 template <int EMIT, class Src>
 __device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
                                            const uint32_t* __restrict__ offsets, const uint32_t* lut,
-                                           const uint8_t* code_of, const uint8_t* __restrict__ sm,
+                                           const uint8_t* __restrict__ sm,
                                            const uint2* __restrict__ meta, void* __restrict__ out, int cols) {
   uint32_t pa = offsets[ca] - base * 32;
   uint32_t pb = has_b ? offsets[cb] - base * 32 : pa;
@@ -138,15 +153,16 @@ __device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, i
         if (has_b) nb = *(const u32x4*)(sm + cb * 256 + (run + 1) * 16);
       }
     }
-    uint32_t ea[4] = {0u, 0u, 0u, 0u}, eb[4] = {0u, 0u, 0u, 0u};
+    constexpr int BITS = EMIT == EMIT_NIBBLE ? 4 : 8, RD = 16 * BITS / 32;
+    uint32_t ea[RD] = {}, eb[RD] = {};
     int ka = 0, kb = 0;
     for (int it = 0; it < 16; ++it) {
-      step(src, pa, qa, ea, ka, lut);
-      step(src, pb, qb, eb, kb, lut);
-      if (!__any(ka < 4 || kb < 4)) break;  // every run of the wave is complete
+      step<BITS>(src, pa, qa, ea, ka, lut);
+      step<BITS>(src, pb, qb, eb, kb, lut);
+      if (!__any(ka < RD || kb < RD)) break;  // every run of the wave is complete
     }
-    emit_run<EMIT>(ea, ca, run, code_of, sa, rawa, out, cols);
-    if (has_b) emit_run<EMIT>(eb, cb, run, code_of, sb, rawb, out, cols);
+    emit_run<EMIT>(ea, ca, run, sa, rawa, out, cols);
+    if (has_b) emit_run<EMIT>(eb, cb, run, sb, rawb, out, cols);
   }
 }
 
@@ -154,9 +170,8 @@ template <int EMIT>
 __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
     const uint32_t* __restrict__ words, uint64_t total_bits, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ lut_g, const uint8_t* __restrict__ sm, const uint2* __restrict__ meta,
-    const uint8_t* __restrict__ code_of_g, void* __restrict__ out, int64_t nchunks, int cols) {
+    void* __restrict__ out, int64_t nchunks, int cols) {
   __shared__ uint32_t lut[4096];
-  __shared__ uint8_t code_of[256];
   __shared__ uint32_t stage[kStageWords];
   const int64_t c0 = (int64_t)blockIdx.x * kChunksPerBlock;
   const int64_t c_end = c0 + kChunksPerBlock < nchunks ? c0 + kChunksPerBlock : nchunks;
@@ -167,17 +182,16 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   const uint32_t w1 = (uint32_t)(end_bit >> 5) + 4;
   const bool staged = w1 - w0 <= (uint32_t)kStageWords;
   {
-    // The decode table, the palette codes and the 16-byte aligned span of
-    // words [w0 & ~3, w1) go to LDS: every load is issued before the first
-    // store, so the copy costs one memory latency, not one per iteration.
+    // The decode table and the 16-byte aligned span of words [w0 & ~3, w1)
+    // go to LDS: every load is issued before the first store, so the copy
+    // costs one memory latency, not one per iteration.
     constexpr int LV = 4096 * 4 / 16 / kThreads;             // table pieces per thread
     constexpr int SV = (kStageWords / 4 + 2 + kThreads - 1) / kThreads;  // stream pieces per thread
     const rsrc_t rs_lut = make_rsrc(lut_g, 4096 * 4);
     const rsrc_t rs_words = make_rsrc(words, (((total_bits + 31) >> 5) + kStreamPad) * 4);
-    const rsrc_t rs_code = make_rsrc(code_of_g, 256);
     const uint32_t a0 = w0 & ~3u;
     const uint32_t nvec = staged ? (w1 - a0 + 3) / 4 : 0u;
-    u32x4 lv[LV], sv[SV], cv;
+    u32x4 lv[LV], sv[SV];
 #pragma unroll
     for (int k = 0; k < LV; ++k) lv[k] = ld16(rs_lut, (threadIdx.x + k * kThreads) * 16, 0);
 #pragma unroll
@@ -185,10 +199,8 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
       const uint32_t i = threadIdx.x + k * kThreads;
       sv[k] = ld16(rs_words, i < nvec ? (a0 + 4 * i) * 4 : kOffRange, 0);
     }
-    cv = ld16(rs_code, EMIT == EMIT_NIBBLE && threadIdx.x < 16 ? threadIdx.x * 16 : kOffRange, 0);
 #pragma unroll
     for (int k = 0; k < LV; ++k) ((u32x4*)lut)[threadIdx.x + k * kThreads] = lv[k];
-    if (EMIT == EMIT_NIBBLE && threadIdx.x < 16) ((u32x4*)code_of)[threadIdx.x] = cv;
 #pragma unroll
     for (int k = 0; k < SV; ++k) {
       const uint32_t i = threadIdx.x + k * kThreads;
@@ -207,10 +219,10 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   const bool has_b = cb < nchunks;
   if (staged) {
     auto src = [&](uint32_t i) { return stage[i]; };
-    decode_two<EMIT>(src, w0, ca, cb, has_b, offsets, lut, code_of, sm, meta, out, cols);
+    decode_two<EMIT>(src, w0, ca, cb, has_b, offsets, lut, sm, meta, out, cols);
   } else {
     auto src = [&](uint32_t i) { return words[i]; };
-    decode_two<EMIT>(src, 0u, ca, cb, has_b, offsets, lut, code_of, sm, meta, out, cols);
+    decode_two<EMIT>(src, 0u, ca, cb, has_b, offsets, lut, sm, meta, out, cols);
   }
 }
 
@@ -220,8 +232,8 @@ hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipS
   const int64_t nchunks = h.rows * h.cols / 256;
   const dim3 grid((unsigned)((nchunks + kChunksPerBlock - 1) / kChunksPerBlock));
 #define UW_LAUNCH(E)                                                                                          \
-  hipLaunchKernelGGL(huff_decode_kernel<E>, grid, dim3(kThreads), 0, s, h.words, h.total_bits, h.offsets, h.lut, \
-                     h.sm, h.meta, h.code_of, out, nchunks, (int)h.cols)
+  hipLaunchKernelGGL(huff_decode_kernel<E>, grid, dim3(kThreads), 0, s, h.words, h.total_bits, h.offsets,          \
+                     E == EMIT_NIBBLE ? h.lut_codes : h.lut, h.sm, h.meta, out, nchunks, (int)h.cols)
   switch (emit) {
     case EMIT_BF16: UW_LAUNCH(EMIT_BF16); break;
     case EMIT_EXP: UW_LAUNCH(EMIT_EXP); break;

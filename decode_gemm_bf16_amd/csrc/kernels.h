@@ -55,6 +55,7 @@ struct HuffDev {
   const uint32_t* words;
   const uint32_t* offsets;
   const uint32_t* lut;      // 4096 entries: up to 3 symbols | count << 24 | bits << 26
+  const uint32_t* lut_codes;  // EMIT_NIBBLE: the same with 4-bit palette codes (bits 0-11) instead of symbols
   const uint8_t* sm;        // EMIT_BF16
   const uint2* meta;        // EMIT_NIBBLE: per-brick raw map
   const uint8_t* code_of;   // EMIT_NIBBLE: 256 entries, code of each palette exponent

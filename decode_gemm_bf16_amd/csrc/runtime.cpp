@@ -143,6 +143,7 @@ struct uw_matrix {
   uint32_t* d_words = nullptr;
   uint32_t* d_offsets = nullptr;
   uint32_t* d_lut = nullptr;  // multi-symbol decode table (4096 entries)
+  uint32_t* d_lut_codes = nullptr;  // the same with 4-bit palette codes (palette tables present)
   uint32_t lut_v[4] = {};
   uint64_t words_total = 0;  // payload + padding words on the device
   hipStream_t main = nullptr, side = nullptr;
@@ -195,6 +196,7 @@ uw::HuffDev huff_view(const uw_matrix* h) {
   d.words = h->d_words;
   d.offsets = h->d_offsets;
   d.lut = h->d_lut;
+  d.lut_codes = h->d_lut_codes;
   d.sm = h->d_sm;
   d.meta = h->d_meta;
   d.code_of = h->d_code_of;
@@ -331,7 +333,7 @@ uw_status upload(uw_matrix* h) {
   const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
   if (pal) total += align256(n / 2);
   if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64)) + align256(256);
-  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + align256(uw::kLutSize * 4);
+  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + 2 * align256(uw::kLutSize * 4);
   if (hipMalloc(&h->dmem, total) != hipSuccess) {
     h->dmem = nullptr;
     return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", total);
@@ -370,6 +372,16 @@ uw_status upload(uw_matrix* h) {
     const std::vector<uint32_t> lut3 = uw::multi_symbol_table(f.lut);
     h->d_lut = carve<uint32_t>(cur, uw::kLutSize * 4);
     UW_HIP(hipMemcpy(h->d_lut, lut3.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
+    // pipeline 3 decodes straight to palette codes
+    uint8_t code_of[256];
+    std::memset(code_of, 0, sizeof code_of);
+    if (tabs) {
+      const int used = std::min<int>(16, int(f.distinct));
+      for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
+    }
+    const std::vector<uint32_t> lutc = uw::multi_code_table(lut3, code_of);
+    h->d_lut_codes = carve<uint32_t>(cur, uw::kLutSize * 4);
+    UW_HIP(hipMemcpy(h->d_lut_codes, lutc.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
     h->words_total = f.words.size();
   }
   if (tabs) {
@@ -689,6 +701,7 @@ uw_status uw_clone(uw_handle h, uw_handle* out) {
   c->d_words = rebase(h->d_words);
   c->d_offsets = rebase(h->d_offsets);
   c->d_lut = rebase(h->d_lut);
+  c->d_lut_codes = rebase(h->d_lut_codes);
   if (hipMemcpy(c->dmem, h->dmem, h->dmem_bytes, hipMemcpyDeviceToDevice) != hipSuccess ||
       hipEventCreateWithFlags(&c->prep_done, hipEventDisableTiming) != hipSuccess) {
     (void)hipFree(c->dmem);
