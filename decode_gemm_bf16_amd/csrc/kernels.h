@@ -58,7 +58,6 @@ struct HuffDev {
   const uint32_t* lut_codes;  // EMIT_NIBBLE: the same with 4-bit palette codes (bits 0-11) instead of symbols
   const uint8_t* sm;        // EMIT_BF16
   const uint2* meta;        // EMIT_NIBBLE: per-brick raw map
-  const uint8_t* code_of;   // EMIT_NIBBLE: 256 entries, code of each palette exponent
   uint64_t total_bits;      // payload bits of the stream (words holds 8 zero words more)
   int64_t rows, cols;
 };

@@ -139,7 +139,6 @@ struct uw_matrix {
   uint8_t* d_nib = nullptr;
   uint2* d_meta = nullptr;
   uint8_t* d_side = nullptr;
-  uint8_t* d_code_of = nullptr;
   uint32_t* d_words = nullptr;
   uint32_t* d_offsets = nullptr;
   uint32_t* d_lut = nullptr;  // multi-symbol decode table (4096 entries)
@@ -199,7 +198,6 @@ uw::HuffDev huff_view(const uw_matrix* h) {
   d.lut_codes = h->d_lut_codes;
   d.sm = h->d_sm;
   d.meta = h->d_meta;
-  d.code_of = h->d_code_of;
   d.total_bits = h->hf.stream_bits;
   d.rows = h->rows;
   d.cols = h->cols;
@@ -332,7 +330,7 @@ uw_status upload(uw_matrix* h) {
   size_t total = align256(n);  // sm
   const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
   if (pal) total += align256(n / 2);
-  if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64)) + align256(256);
+  if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64));
   if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + 2 * align256(uw::kLutSize * 4);
   if (hipMalloc(&h->dmem, total) != hipSuccess) {
     h->dmem = nullptr;
@@ -355,14 +353,6 @@ uw_status upload(uw_matrix* h) {
     UW_HIP(hipMemcpy(h->d_meta, meta.data(), nb * 8, hipMemcpyHostToDevice));
     h->d_side = carve<uint8_t>(cur, std::max<size_t>(f.side.size(), 64));
     if (!f.side.empty()) UW_HIP(hipMemcpy(h->d_side, f.side.data(), f.side.size(), hipMemcpyHostToDevice));
-    uint8_t code_of[256];
-    std::memset(code_of, 0, sizeof code_of);
-    if (tabs) {
-      const int used = std::min<int>(16, int(f.distinct));
-      for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
-    }
-    h->d_code_of = carve<uint8_t>(cur, 256);
-    UW_HIP(hipMemcpy(h->d_code_of, code_of, 256, hipMemcpyHostToDevice));
   }
   if (huf) {
     h->d_words = carve<uint32_t>(cur, f.words.size() * 4);
@@ -697,7 +687,6 @@ uw_status uw_clone(uw_handle h, uw_handle* out) {
   c->d_nib = rebase(h->d_nib);
   c->d_meta = rebase(h->d_meta);
   c->d_side = rebase(h->d_side);
-  c->d_code_of = rebase(h->d_code_of);
   c->d_words = rebase(h->d_words);
   c->d_offsets = rebase(h->d_offsets);
   c->d_lut = rebase(h->d_lut);

@@ -88,10 +88,13 @@ def _serial_from_interleaved(buf, n, run_bytes):
     return runs[slot.reshape(-1)].reshape(-1)[: n * run_bytes // 16]
 
 
-def test_preprocess_streams_bit_exact(env):
-    """Pipeline 2's exponent bytes and pipeline 3's 4-bit codes equal the oracle's."""
+@pytest.mark.parametrize("data", ["ragged", "patterns"])
+def test_preprocess_streams_bit_exact(env, data):
+    """Pipeline 2's exponent bytes and pipeline 3's 4-bit codes equal the
+    oracle's -- on low-entropy weights (stream staged in LDS) and on all 65,536
+    bit patterns (8 bits per exponent: the stream is read from global memory)."""
     torch, uw = env
-    w = synth.weights(272, 576, 5, 0.004, 12)
+    w = synth.weights(272, 576, 5, 0.004, 12) if data == "ragged" else synth.all_bf16_patterns(1)
     m = _both(env, w)
     inf = m.info()
     e_serial = oracle.to_serial(oracle.split(w)[0])
