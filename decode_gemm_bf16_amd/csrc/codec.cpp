@@ -260,13 +260,19 @@ std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut) {
   return out;
 }
 
-std::vector<uint32_t> multi_code_table(const std::vector<uint32_t>& multi, const uint8_t code_of[256]) {
-  std::vector<uint32_t> out(multi.size());
-  for (size_t p = 0; p < multi.size(); ++p) {
-    const uint32_t e = multi[p], cnt = (e >> 24) & 3u;
-    uint32_t codes = 0;
-    for (uint32_t i = 0; i < cnt; ++i) codes |= uint32_t(code_of[(e >> (8 * i)) & 0xFFu] & 0xFu) << (4 * i);
-    out[p] = codes | (e & 0xFF000000u);
+std::vector<uint32_t> multi_code_table(const std::vector<uint16_t>& lut, const uint8_t code_of[256]) {
+  std::vector<uint32_t> out(kLutSize, 0);
+  for (uint32_t p = 0; p < uint32_t(kLutSize); ++p) {
+    uint32_t codes = 0, cnt = 0, pos = 0;
+    while (cnt < 5) {
+      const uint16_t e = lut[(p << pos) & uint32_t(kLutSize - 1)];
+      const uint32_t len = e >> 8;
+      if (len == 0 || pos + len > uint32_t(kLmax)) break;
+      codes |= uint32_t(code_of[e & 0xFF] & 0xFu) << (4 * cnt);
+      ++cnt;
+      pos += len;
+    }
+    out[p] = codes | (cnt << 24) | (pos << 27);
   }
   return out;
 }

@@ -60,11 +60,12 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
 // the bits they take.  Built from the one-symbol table `lut`.
 std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut);
 
-// The multi-symbol table with each symbol replaced by its 4-bit palette code
-// (code_of[symbol]; symbols outside the palette, which only occur in raw
-// groups, get 0): bits 0-11 the codes (first in the low nibble), count and
-// bits as in multi_symbol_table.
-std::vector<uint32_t> multi_code_table(const std::vector<uint32_t>& multi, const uint8_t code_of[256]);
+// Decode table for pipeline 3: for each 12-bit window, the 4-bit palette
+// codes (code_of[symbol]; symbols outside the palette, which only occur in
+// raw groups, get 0) of the whole codes it starts with, greedily and at most
+// five: bits 0-19 the codes (first in the low nibble), bits 24-26 their count,
+// bits 27-31 the bits they take.
+std::vector<uint32_t> multi_code_table(const std::vector<uint16_t>& lut, const uint8_t code_of[256]);
 
 // Length-limited optimal code lengths over a 256-symbol histogram.
 void limited_code_lengths(const uint64_t hist[256], int lmax, uint8_t lengths[256]);

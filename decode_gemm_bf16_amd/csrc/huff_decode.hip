@@ -5,164 +5,263 @@
 // (pipeline 1), the exponent bytes only (pipeline 2, half the write traffic)
 // or a transcode to 4-bit palette codes (pipeline 3, a quarter).
 //
-// A lane decodes two chunks of 256 symbols each, from their bit offsets, in
-// lockstep (two independent dependency chains per lane).  Decoding is a chain
-// of dependent table lookups -- the position of a code is known only once the
-// previous one is decoded -- so its time is the chain's length times the LDS
-// round trip.  The 12-bit code limit lets one 4096-entry table in LDS decode,
-// from the 12 bits at the chain's bit position, every whole code those bits
-// hold, up to three: with exponent codes of 2-3 bits on average a lookup
-// yields about three symbols, a third of the chain.  A step reads the two
-// stream words around the position (one LDS instruction) and shifts out a
-// 32-bit window -- no bit buffer to refill -- and every step is branch-free,
-// so a wave whose lanes are at different points of their runs runs one
-// instruction stream.  Symbols gather in a 64-bit queue per chunk; a run (16
-// symbols) is emitted once both chains of every lane of the wave hold one.
-// Pipeline 3 uses a second table whose entries hold the symbols' 4-bit palette
-// codes, so the transcode is a nibble shuffle per 8 codes.
-// The 256 chunks of a workgroup are consecutive in the stream, so their bits
-// are first copied into LDS with coalesced 16-byte loads.  (A workgroup whose
-// span does not fit, which needs about 3 bits per exponent on average, reads
-// its words from global memory.)
+// A lane decodes two chunks of 256 symbols, from their bit offsets, in
+// lockstep (two independent dependency chains per lane); a workgroup of four
+// waves takes 512 consecutive chunks.  The code-length limit of 12 bits lets
+// one 4096-entry table in LDS decode, from the 12 bits at a chain's position,
+// every whole code those bits start with: up to three exponent symbols
+// (pipelines 1, 2; about 2.9 a lookup on exponent statistics) or up to five
+// 4-bit palette codes (pipeline 3; about 4.2).  Each chain keeps the two
+// stream words around its position in registers and requests the next word
+// one step ahead, so a lookup waits for one LDS round trip; a word moves in
+// after every second lookup (two lookups take at most 24 bits).  All steps
+// are branch-free, so a wave whose lanes are at different points of their
+// runs runs one instruction stream.
+//
+// Decoded symbols go to a small per-chunk slot in LDS: exponent symbols as
+// bytes (three byte stores a lookup: an unaligned dword store stalls the
+// LDS), palette codes through a 64-bit register queue whose low dword is
+// stored, aligned, after every lookup.  A run (16 symbols) is emitted once
+// both chains of every lane of the wave hold one; a chain may run up to half
+// a run ahead.  The 512 chunks' bits are first copied into LDS with
+// coalesced 16-byte loads (a workgroup whose span does not fit, which needs
+// more than 2.8 bits per exponent on average -- 3.3 for pipeline 3 -- reads
+// its words from global memory).
 //
 // A chunk is a quarter brick: 16 runs of 16 symbols, run i = row i of the
-// brick, 16 consecutive columns.  All lanes of a wave emit a run in the same
-// step; for the bf16 output consecutive lanes write consecutive 32-byte
-// pieces of one output row.
+// brick, 16 consecutive columns.  Pipelines 2 and 3 write run r of chunk c at
+// slot ((c / 512) * 16 + r) * 512 + c % 512: the workgroup's 512 chunks store
+// one run as one contiguous block, and the blocks of successive runs follow
+// each other.  Pipeline 1 writes bf16 W row-major.
 #include "kernels.h"
 #include "recon.h"
 
 namespace uw {
 namespace {
 
-constexpr int kChunksPerBlock = 256;
-constexpr int kThreads = 128;      // two chunks per lane
-constexpr int kStreamPad = 8;      // zero words after the stream (the encoder's padding)
-constexpr int kStageWords = 6016;  // 23.5 KB of staged bitstream: with the 16 KB table, 4 workgroups per CU
+constexpr int kThreads = 256;                   // four waves, two chunks per lane
+constexpr int kChunksPerBlock = 2 * kThreads;   // the interleave group of the scratch order
+constexpr int kStreamPad = 8;                   // zero words after the stream (the encoder's padding)
+constexpr int kSymSlot = 36;                    // bytes per chunk (9 dwords: the lanes' slots start in distinct banks)
+constexpr uint32_t kSymLead = 24;               // a pair of lookups is taken while a slot holds fewer symbols
+constexpr int kCodeSlot = 5;                    // dwords per chunk for palette codes
+constexpr uint32_t kCodeLead = 3;               // a pair is taken while fewer dwords are full
 
-// The next 32 bits of the stream from bit `pos` (MSB first): two consecutive
-// words and a 64-bit shift.
-template <class Src>
-__device__ __forceinline__ uint32_t window(Src src, uint32_t pos) {
-  const uint32_t wi = pos >> 5;
-  const uint64_t two = ((uint64_t)src(wi) << 32) | src(wi + 1);
-  return (uint32_t)((two << (pos & 31)) >> 32);
+// Staged bitstream, in words: LDS per workgroup = 16 KB table + stage + slots,
+// two workgroups per CU.
+template <int EMIT>
+constexpr int stage_words() {
+  return EMIT == EMIT_NIBBLE ? 13568 : 11520;
 }
 
-// Symbols (or 4-bit codes) decoded but not yet placed in a run, first in the
-// low bits.
-struct Queue {
-  uint64_t q;
-  int n;
+__device__ __forceinline__ void st8(rsrc_t r, u32x2 v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void st16(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
+}
+
+// A chain's place in the stream: the words holding bits [32*wb, 32*wb + 64),
+// the position kept as r = 50 - (offset in them) so that one 64-bit right
+// shift puts the 12-bit window, times 4 (a table byte offset), at bits 2-13,
+// and the next word, requested ahead.  r >= 7 at a lookup (offset <= 43),
+// r >= -5 after the second of a pair.
+struct BitBuf {
+  uint32_t b0, b1, nw, wb;
+  int32_t r;
 };
 
-// One chain step, branch-free.  BITS = 8: the table yields exponent symbols;
-// BITS = 4: it yields their palette codes (pipeline 3).  A lookup on the 12
-// bits at `pos` appends its 1 to 3 entries to the queue when the queue holds
-// less than a dword (else the entry is dropped and nothing moves); then a
-// dword of queued entries moves into the run being built when the run is not
-// complete -- the run's dwords shift down one place and the new one enters
-// last, so they end in order.
-template <int BITS, class Src>
-__device__ __forceinline__ void step(Src src, uint32_t& pos, Queue& qu, uint32_t* e, int& k, const uint32_t* lut) {
-  constexpr int PER = 32 / BITS;       // entries per dword
-  constexpr int RD = 16 * BITS / 32;   // dwords per run
-  constexpr uint32_t MASK = BITS == 8 ? 0xFFFFFFu : 0xFFFu;
-  uint32_t ent = lut[window(src, pos) >> 20];
-  ent = qu.n < PER ? ent : 0u;
-  pos += ent >> 26;
-  qu.q |= (uint64_t)(ent & MASK) << (BITS * qu.n);
-  qu.n += (int)((ent >> 24) & 3u);
-  const bool mv = qu.n >= PER && k < RD;
-  if constexpr (RD == 4) {
-    e[0] = mv ? e[1] : e[0];
-    e[1] = mv ? e[2] : e[1];
-    e[2] = mv ? e[3] : e[2];
-    e[3] = mv ? (uint32_t)qu.q : e[3];
-  } else {
-    e[0] = mv ? e[1] : e[0];
-    e[1] = mv ? (uint32_t)qu.q : e[1];
-  }
-  qu.q = mv ? qu.q >> 32 : qu.q;
-  qu.n -= mv ? PER : 0;
-  k += mv ? 1 : 0;
+template <class Src>
+__device__ __forceinline__ void bits_init(Src src, uint32_t pos, BitBuf& bb) {
+  bb.wb = pos >> 5;
+  bb.r = 50 - (int32_t)(pos & 31);
+  bb.b0 = src(bb.wb);
+  bb.b1 = src(bb.wb + 1);
+  bb.nw = src(bb.wb + 2);
 }
 
-template <int EMIT>
-__device__ __forceinline__ void emit_run(const uint32_t* ew, int64_t c, int run, const u32x4& s, uint32_t rawmap,
-                                         void* __restrict__ out, int cols) {
-  // exponent bytes and 4-bit codes go to the interleaved scratch order (runs
-  // of 64 consecutive chunks side by side, see code_lane_off in recon.h): the
-  // 64 lanes of a wave, 64 consecutive chunks, store one run as one
-  // contiguous block instead of 64 pieces 256 bytes apart
-  const int64_t ilv_run = ((c >> 6) * 16 + run) * 64 + (c & 63);
-  if (EMIT == EMIT_EXP) {
-    *(u32x4*)((uint8_t*)out + ilv_run * 16) = u32x4{ew[0], ew[1], ew[2], ew[3]};
-  } else if (EMIT == EMIT_NIBBLE) {
-    // ew[0..1]: the run's 16 codes in order, 8 per dword (code i at bits 4i);
-    // stored form: of 8 codes, byte b = code b | code b+4 << 4
-    uint32_t nw[2] = {0u, 0u};
-    if (!((rawmap >> run) & 1u)) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t even = ew[h] & 0x0F0F0F0Fu;         // codes 0,2,4,6
-        const uint32_t odd = (ew[h] >> 4) & 0x0F0F0F0Fu;   // codes 1,3,5,7
-        const uint32_t first = __builtin_amdgcn_perm(odd, even, 0x05010400u);   // codes 0..3
-        const uint32_t second = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // codes 4..7
-        nw[h] = first | (second << 4);
-      }
-    }
-    *(u32x2*)((uint8_t*)out + ilv_run * 8) = u32x2{nw[0], nw[1]};
-  } else {
-    uint32_t p[8];
-    rebuild_exp(s, u32x4{ew[0], ew[1], ew[2], ew[3]}, p);
-    const int kbn = cols >> 6;
-    const int64_t brick = c >> 2, tb = brick / kbn, kb = brick % kbn;
-    uint16_t* o = (uint16_t*)out + (tb * 16 + run) * (int64_t)cols + kb * 64 + (c & 3) * 16;
-    *(u32x4*)o = u32x4{p[0], p[1], p[2], p[3]};
-    *(u32x4*)(o + 8) = u32x4{p[4], p[5], p[6], p[7]};
-  }
+__device__ __forceinline__ uint32_t table_entry(const BitBuf& bb, const uint8_t* lut) {
+  const uint64_t two = ((uint64_t)bb.b0 << 32) | bb.b1;
+  return *(const uint32_t*)(lut + ((uint32_t)(two >> bb.r) & 0x3FFCu));
 }
 
-// Two chunks per lane, decoded in lockstep: their lookups are independent, so
-// one chain's LDS latency hides behind the other's.  A run needs at most 16
-// steps (each step's lookup yields at least one symbol), which bounds the
-// loop; the wave leaves it as soon as every run of the wave is complete.
+// After a pair of lookups: move on by a word if the position left b0, and
+// request the word after the new b1.
+template <class Src>
+__device__ __forceinline__ void refill(Src src, BitBuf& bb) {
+  const bool adv = bb.r <= 18;
+  bb.b0 = adv ? bb.b1 : bb.b0;
+  bb.b1 = adv ? bb.nw : bb.b1;
+  bb.r += adv ? 32 : 0;
+  bb.wb += adv ? 1u : 0u;
+  bb.nw = src(bb.wb + 2);
+}
+
+// Exponent symbols: an entry holds up to three symbols (bits 0-23), their
+// count (24-25) and the bits they take (26-29); they are appended to the slot
+// at p (an entry not taken appends nothing and leaves the position).
+__device__ __forceinline__ void lookup_sym(BitBuf& bb, uint32_t& p, bool take, uint8_t* slot, const uint8_t* lut) {
+  uint32_t ent = table_entry(bb, lut);
+  ent = take ? ent : 0u;
+  bb.r -= (int32_t)(ent >> 26);
+  slot[p] = (uint8_t)ent;
+  slot[p + 1] = (uint8_t)(ent >> 8);
+  slot[p + 2] = (uint8_t)(ent >> 16);
+  p += (ent >> 24) & 3u;
+}
+
+// The run's 16 symbols; the ones decoded past it move to the slot's start.
+__device__ __forceinline__ u32x4 take_sym_run(uint8_t* slot, uint32_t& p) {
+  uint32_t* w = (uint32_t*)slot;
+  const u32x4 e = {w[0], w[1], w[2], w[3]};
+  const uint32_t r0 = w[4], r1 = w[5], r2 = w[6], r3 = w[7];
+  w[0] = r0;
+  w[1] = r1;
+  w[2] = r2;
+  w[3] = r3;
+  p -= 16;
+  return e;
+}
+
+// Palette codes: an entry holds up to five codes (bits 0-19), their count
+// (24-26) and the bits they take (27-31).  They join the queue; its low dword
+// is stored at dword k of the slot and k moves on once the dword holds 8.
+struct CodeQ {
+  uint64_t q;
+  uint32_t qn, k;
+};
+
+__device__ __forceinline__ void lookup_code(BitBuf& bb, CodeQ& cq, bool take, uint32_t* slot, const uint8_t* lut) {
+  uint32_t ent = table_entry(bb, lut);
+  ent = take ? ent : 0u;
+  bb.r -= (int32_t)(ent >> 27);
+  cq.q |= (uint64_t)(ent & 0xFFFFFu) << (4 * cq.qn);
+  cq.qn += (ent >> 24) & 7u;
+  slot[cq.k] = (uint32_t)cq.q;
+  const bool mv = cq.qn >= 8u;
+  cq.q = mv ? cq.q >> 32 : cq.q;
+  cq.qn -= mv ? 8u : 0u;
+  cq.k += mv ? 1u : 0u;
+}
+
+// Pipeline 2 and 3 store offset of chunk c's run 0 (bytes; run r adds
+// r * 512 * S), S bytes per run.
+__device__ __forceinline__ uint32_t ilv_lane(int64_t c, uint32_t S) {
+  return (uint32_t)(((c >> 9) * (16 * kChunksPerBlock) + (c & (kChunksPerBlock - 1))) * S);
+}
+
 template <int EMIT, class Src>
-__device__ __forceinline__ void decode_two(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
-                                           const uint32_t* __restrict__ offsets, const uint32_t* lut,
-                                           const uint8_t* __restrict__ sm,
-                                           const uint2* __restrict__ meta, void* __restrict__ out, int cols) {
-  uint32_t pa = offsets[ca] - base * 32;
-  uint32_t pb = has_b ? offsets[cb] - base * 32 : pa;
-  const uint32_t rawa = EMIT == EMIT_NIBBLE ? meta[ca >> 2].x : 0u;
-  const uint32_t rawb = (EMIT == EMIT_NIBBLE && has_b) ? meta[cb >> 2].x : 0u;
-  Queue qa = {0ull, 0}, qb = {0ull, 0};
+__device__ __forceinline__ void decode_sym(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
+                                           const uint32_t* __restrict__ offsets, const uint8_t* lut,
+                                           uint8_t* slot_a, uint8_t* slot_b, const uint8_t* __restrict__ sm,
+                                           void* __restrict__ out, uint64_t out_bytes, int cols) {
+  BitBuf ba, bb;
+  bits_init(src, offsets[ca] - base * 32, ba);
+  bits_init(src, has_b ? offsets[cb] - base * 32 : offsets[ca] - base * 32, bb);
+  uint32_t na = 0, nb = 0;
+  const rsrc_t rs_out = make_rsrc(out, out_bytes);
+  const uint32_t va = ilv_lane(ca, 16), vb = ilv_lane(cb, 16);
   // bf16 output: the run's sign+mantissa bytes, requested one run ahead
-  u32x4 sa = {0u, 0u, 0u, 0u}, sb = {0u, 0u, 0u, 0u}, na = sa, nb = sb;
+  u32x4 sa = {0u, 0u, 0u, 0u}, sb = sa, ta = sa, tb = sa;
   if (EMIT == EMIT_BF16) {
-    na = *(const u32x4*)(sm + ca * 256);
-    if (has_b) nb = *(const u32x4*)(sm + cb * 256);
+    ta = *(const u32x4*)(sm + ca * 256);
+    if (has_b) tb = *(const u32x4*)(sm + cb * 256);
   }
   for (int run = 0; run < 16; ++run) {
     if (EMIT == EMIT_BF16) {
-      sa = na;
-      sb = nb;
+      sa = ta;
+      sb = tb;
       if (run + 1 < 16) {
-        na = *(const u32x4*)(sm + ca * 256 + (run + 1) * 16);
-        if (has_b) nb = *(const u32x4*)(sm + cb * 256 + (run + 1) * 16);
+        ta = *(const u32x4*)(sm + ca * 256 + (run + 1) * 16);
+        if (has_b) tb = *(const u32x4*)(sm + cb * 256 + (run + 1) * 16);
       }
     }
-    constexpr int BITS = EMIT == EMIT_NIBBLE ? 4 : 8, RD = 16 * BITS / 32;
-    uint32_t ea[RD] = {}, eb[RD] = {};
-    int ka = 0, kb = 0;
-    for (int it = 0; it < 16; ++it) {
-      step<BITS>(src, pa, qa, ea, ka, lut);
-      step<BITS>(src, pb, qb, eb, kb, lut);
-      if (!__any(ka < RD || kb < RD)) break;  // every run of the wave is complete
+    // every taken lookup yields a symbol, so 8 pairs complete any run
+    for (int it = 0; it < 8; ++it) {
+      const bool take_a = na < kSymLead, take_b = nb < kSymLead;
+      lookup_sym(ba, na, take_a, slot_a, lut);
+      lookup_sym(bb, nb, take_b, slot_b, lut);
+      lookup_sym(ba, na, take_a, slot_a, lut);
+      lookup_sym(bb, nb, take_b, slot_b, lut);
+      refill(src, ba);
+      refill(src, bb);
+      if (!__any(na < 16u || nb < 16u)) break;
     }
-    emit_run<EMIT>(ea, ca, run, sa, rawa, out, cols);
-    if (has_b) emit_run<EMIT>(eb, cb, run, sb, rawb, out, cols);
+    const u32x4 ea = take_sym_run(slot_a, na);
+    const u32x4 eb = take_sym_run(slot_b, nb);
+    if (EMIT == EMIT_EXP) {
+      st16(rs_out, ea, va, (uint32_t)run * (16u * kChunksPerBlock));
+      if (has_b) st16(rs_out, eb, vb, (uint32_t)run * (16u * kChunksPerBlock));
+    } else {
+      // bf16: lanes with consecutive chunks write consecutive 32-byte pieces
+      // of one output row
+      const int kbn = cols >> 6;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !has_b) break;
+        const int64_t c = h ? cb : ca;
+        uint32_t p[8];
+        rebuild_exp(h ? sb : sa, h ? eb : ea, p);
+        const int64_t brick = c >> 2, tr = brick / kbn, kb = brick % kbn;
+        uint16_t* o = (uint16_t*)out + (tr * 16 + run) * (int64_t)cols + kb * 64 + (c & 3) * 16;
+        *(u32x4*)o = u32x4{p[0], p[1], p[2], p[3]};
+        *(u32x4*)(o + 8) = u32x4{p[4], p[5], p[6], p[7]};
+      }
+    }
+  }
+}
+
+// a run's 16 codes (code i at bits 4i of d0:d1) in the stored form -- of 8
+// codes, byte b = code b | code b+4 << 4 -- or zeros for a raw row
+__device__ __forceinline__ u32x2 stored_codes(uint32_t d0, uint32_t d1, bool raw) {
+  const uint32_t d[2] = {d0, d1};
+  uint32_t nw[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t even = d[h] & 0x0F0F0F0Fu;        // codes 0,2,4,6
+    const uint32_t odd = (d[h] >> 4) & 0x0F0F0F0Fu;  // codes 1,3,5,7
+    const uint32_t first = __builtin_amdgcn_perm(odd, even, 0x05010400u);   // codes 0..3
+    const uint32_t second = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // codes 4..7
+    nw[h] = raw ? 0u : (first | (second << 4));
+  }
+  return u32x2{nw[0], nw[1]};
+}
+
+template <class Src>
+__device__ __forceinline__ void decode_codes(Src src, uint32_t base, int64_t ca, int64_t cb, bool has_b,
+                                             const uint32_t* __restrict__ offsets, const uint8_t* lut,
+                                             uint32_t* slot_a, uint32_t* slot_b, const uint2* __restrict__ meta,
+                                             void* __restrict__ out, uint64_t out_bytes) {
+  BitBuf ba, bb;
+  bits_init(src, offsets[ca] - base * 32, ba);
+  bits_init(src, has_b ? offsets[cb] - base * 32 : offsets[ca] - base * 32, bb);
+  // raw rows of the brick: their codes are stored as zeros
+  const uint32_t rawa = meta[ca >> 2].x;
+  const uint32_t rawb = has_b ? meta[cb >> 2].x : 0u;
+  CodeQ qa = {0ull, 0u, 0u}, qb = {0ull, 0u, 0u};
+  const rsrc_t rs_out = make_rsrc(out, out_bytes);
+  const uint32_t va = ilv_lane(ca, 8), vb = ilv_lane(cb, 8);
+  for (int run = 0; run < 16; ++run) {
+    for (int it = 0; it < 8; ++it) {
+      const bool take_a = qa.k < kCodeLead, take_b = qb.k < kCodeLead;
+      lookup_code(ba, qa, take_a, slot_a, lut);
+      lookup_code(bb, qb, take_b, slot_b, lut);
+      lookup_code(ba, qa, take_a, slot_a, lut);
+      lookup_code(bb, qb, take_b, slot_b, lut);
+      refill(src, ba);
+      refill(src, bb);
+      if (!__any(qa.k < 2u || qb.k < 2u)) break;
+    }
+    const uint32_t a0 = slot_a[0], a1 = slot_a[1], a2 = slot_a[2], a3 = slot_a[3];
+    const uint32_t b0 = slot_b[0], b1 = slot_b[1], b2 = slot_b[2], b3 = slot_b[3];
+    slot_a[0] = a2;
+    slot_a[1] = a3;
+    slot_b[0] = b2;
+    slot_b[1] = b3;
+    qa.k -= 2u;
+    qb.k -= 2u;
+    st8(rs_out, stored_codes(a0, a1, (rawa >> run) & 1u), va, (uint32_t)run * (8u * kChunksPerBlock));
+    if (has_b) st8(rs_out, stored_codes(b0, b1, (rawb >> run) & 1u), vb, (uint32_t)run * (8u * kChunksPerBlock));
   }
 }
 
@@ -170,23 +269,27 @@ template <int EMIT>
 __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
     const uint32_t* __restrict__ words, uint64_t total_bits, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ lut_g, const uint8_t* __restrict__ sm, const uint2* __restrict__ meta,
-    void* __restrict__ out, int64_t nchunks, int cols) {
+    void* __restrict__ out, uint64_t out_bytes, int64_t nchunks, int cols) {
+  constexpr int kStage = stage_words<EMIT>();
+  constexpr int kSlotBytes = EMIT == EMIT_NIBBLE ? kCodeSlot * 4 : kSymSlot;
   __shared__ uint32_t lut[4096];
-  __shared__ uint32_t stage[kStageWords];
+  __shared__ uint32_t stage[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kChunksPerBlock * kSlotBytes];
   const int64_t c0 = (int64_t)blockIdx.x * kChunksPerBlock;
   const int64_t c_end = c0 + kChunksPerBlock < nchunks ? c0 + kChunksPerBlock : nchunks;
-  // words that the chunks c0 .. c_end-1 read: from the first chunk's start to
-  // 3 words past the last chunk's end (the bit buffer's look-ahead)
+  // words read: from the first chunk's start to 5 words past the last
+  // chunk's end (a chain keeps taking lookups while its slot has room: at
+  // most 8 of at most 12 bits past its end; the bit buffer reads 2 words
+  // past its position)
   const uint32_t w0 = offsets[c0] >> 5;
   const uint64_t end_bit = c_end < nchunks ? (uint64_t)offsets[c_end] : total_bits;
-  const uint32_t w1 = (uint32_t)(end_bit >> 5) + 4;
-  const bool staged = w1 - w0 <= (uint32_t)kStageWords;
+  const uint32_t w1 = (uint32_t)(end_bit >> 5) + 6;
+  const bool staged = w1 - w0 <= (uint32_t)kStage;
   {
-    // The decode table and the 16-byte aligned span of words [w0 & ~3, w1)
-    // go to LDS: every load is issued before the first store, so the copy
-    // costs one memory latency, not one per iteration.
-    constexpr int LV = 4096 * 4 / 16 / kThreads;             // table pieces per thread
-    constexpr int SV = (kStageWords / 4 + 2 + kThreads - 1) / kThreads;  // stream pieces per thread
+    // The table and the 16-byte aligned span of words [w0 & ~3, w1) go to
+    // LDS: every load is issued before the first store.
+    constexpr int LV = 4096 * 4 / 16 / kThreads;
+    constexpr int SV = (kStage / 4 + 2 + kThreads - 1) / kThreads;
     const rsrc_t rs_lut = make_rsrc(lut_g, 4096 * 4);
     const rsrc_t rs_words = make_rsrc(words, (((total_bits + 31) >> 5) + kStreamPad) * 4);
     const uint32_t a0 = w0 & ~3u;
@@ -208,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const int32_t d = (int32_t)(a0 + 4 * i + kk) - (int32_t)w0;
-          if (d >= 0 && d < kStageWords) stage[d] = sv[k][kk];
+          if (d >= 0 && d < kStage) stage[d] = sv[k][kk];
         }
       }
     }
@@ -217,12 +320,27 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   const int64_t ca = c0 + threadIdx.x, cb = ca + kThreads;
   if (ca >= nchunks) return;
   const bool has_b = cb < nchunks;
-  if (staged) {
-    auto src = [&](uint32_t i) { return stage[i]; };
-    decode_two<EMIT>(src, w0, ca, cb, has_b, offsets, lut, sm, meta, out, cols);
+  const uint8_t* lutb = (const uint8_t*)lut;
+  if constexpr (EMIT == EMIT_NIBBLE) {
+    uint32_t* slot_a = (uint32_t*)slots + threadIdx.x * kCodeSlot;
+    uint32_t* slot_b = (uint32_t*)slots + (threadIdx.x + kThreads) * kCodeSlot;
+    if (staged) {
+      auto src = [&](uint32_t i) { return stage[i]; };
+      decode_codes(src, w0, ca, cb, has_b, offsets, lutb, slot_a, slot_b, meta, out, out_bytes);
+    } else {
+      auto src = [&](uint32_t i) { return words[i]; };
+      decode_codes(src, 0u, ca, cb, has_b, offsets, lutb, slot_a, slot_b, meta, out, out_bytes);
+    }
   } else {
-    auto src = [&](uint32_t i) { return words[i]; };
-    decode_two<EMIT>(src, 0u, ca, cb, has_b, offsets, lut, sm, meta, out, cols);
+    uint8_t* slot_a = slots + threadIdx.x * kSymSlot;
+    uint8_t* slot_b = slots + (threadIdx.x + kThreads) * kSymSlot;
+    if (staged) {
+      auto src = [&](uint32_t i) { return stage[i]; };
+      decode_sym<EMIT>(src, w0, ca, cb, has_b, offsets, lutb, slot_a, slot_b, sm, out, out_bytes, cols);
+    } else {
+      auto src = [&](uint32_t i) { return words[i]; };
+      decode_sym<EMIT>(src, 0u, ca, cb, has_b, offsets, lutb, slot_a, slot_b, sm, out, out_bytes, cols);
+    }
   }
 }
 
@@ -230,10 +348,18 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
 
 hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipStream_t s) {
   const int64_t nchunks = h.rows * h.cols / 256;
-  const dim3 grid((unsigned)((nchunks + kChunksPerBlock - 1) / kChunksPerBlock));
-#define UW_LAUNCH(E)                                                                                          \
+  if (nchunks <= 0) return hipSuccess;
+  // pipelines 2 and 3: the interleaved order pads to whole groups of 512 chunks
+  const uint64_t groups = (uint64_t)(nchunks + kChunksPerBlock - 1) / kChunksPerBlock;
+  const uint64_t out_bytes = emit == EMIT_EXP      ? groups * kChunksPerBlock * 256
+                             : emit == EMIT_NIBBLE ? groups * kChunksPerBlock * 128
+                                                   : (uint64_t)nchunks * 512;
+  // buffer stores take 32-bit offsets within a 2 GB range
+  if (emit != EMIT_BF16 && out_bytes > 0x7FFFFFF0ull) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)groups);
+#define UW_LAUNCH(E)                                                                                           \
   hipLaunchKernelGGL(huff_decode_kernel<E>, grid, dim3(kThreads), 0, s, h.words, h.total_bits, h.offsets,          \
-                     E == EMIT_NIBBLE ? h.lut_codes : h.lut, h.sm, h.meta, out, nchunks, (int)h.cols)
+                     E == EMIT_NIBBLE ? h.lut_codes : h.lut, h.sm, h.meta, out, out_bytes, nchunks, (int)h.cols)
   switch (emit) {
     case EMIT_BF16: UW_LAUNCH(EMIT_BF16); break;
     case EMIT_EXP: UW_LAUNCH(EMIT_EXP); break;

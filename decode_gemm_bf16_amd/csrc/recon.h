@@ -135,15 +135,16 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 // Where run r (row r of the brick) of quarter q of brick b sits in a stream of
 // S bytes per run (exponent bytes: 16, 4-bit codes: 8).  Serial order: run
 // 64b + 16q + r.  Interleaved order, the pipeline 2/3 scratch that the Huffman
-// decoder writes: chunk c = 4b + q (a quarter brick), chunks grouped by 64,
-// run r of chunk c is run (c/64 * 16 + r) * 64 + c%64 -- so that the decoder's
-// 64 lanes, one chunk each, store one run as 64 consecutive pieces.  The
-// offset splits into a per-lane part and a wave-uniform per-brick part.
+// decoder writes: chunk c = 4b + q (a quarter brick), chunks grouped by 512
+// (one decoder workgroup), run r of chunk c is run (c/512 * 16 + r) * 512 +
+// c%512 -- so that the decoder's workgroup stores one run of all its chunks
+// as one contiguous block.  The offset splits into a per-lane part and a
+// wave-uniform per-brick part.
 __device__ __forceinline__ uint32_t code_lane_off(int q, int r, uint32_t S, bool ilv) {
-  return ilv ? (uint32_t)(r * 64 + q) * S : (uint32_t)(q * 16 + r) * S;
+  return ilv ? (uint32_t)(r * 512 + q) * S : (uint32_t)(q * 16 + r) * S;
 }
 __device__ __forceinline__ uint32_t code_brick_off(uint32_t b, uint32_t S, bool ilv) {
-  return ilv ? ((b >> 4) * 1024u + (b & 15u) * 4u) * S : b * 64u * S;
+  return ilv ? ((b >> 7) * 8192u + (b & 127u) * 4u) * S : b * 64u * S;
 }
 
 // A per-lane offset past every range make_rsrc sets: the buffer unit's range

@@ -158,13 +158,13 @@ struct uw_matrix {
   bool has(uint32_t f) const { return (formats & f) != 0; }
   bool has_pal_tables() const { return has(UW_FMT_PALETTE) || has(UW_FMT_RAWAUX); }
   size_t scratch_need(int p) const {
-    // pipelines 2 and 3: the interleaved order pads to whole groups of 64
-    // chunks (64 x 256 weights)
-    const size_t n = size_t(rows) * size_t(cols), groups = (n / 256 + 63) / 64;
+    // pipelines 2 and 3: the interleaved order pads to whole groups of 512
+    // chunks (512 x 256 weights)
+    const size_t n = size_t(rows) * size_t(cols), groups = (n / 256 + 511) / 512;
     switch (p) {
       case 1: return align256(2 * n);
-      case 2: return groups * 64 * 256;
-      case 3: return groups * 64 * 128;
+      case 2: return groups * 512 * 256;
+      case 3: return groups * 512 * 128;
       default: return 0;
     }
   }
@@ -369,7 +369,7 @@ uw_status upload(uw_matrix* h) {
       const int used = std::min<int>(16, int(f.distinct));
       for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
     }
-    const std::vector<uint32_t> lutc = uw::multi_code_table(lut3, code_of);
+    const std::vector<uint32_t> lutc = uw::multi_code_table(f.lut, code_of);
     h->d_lut_codes = carve<uint32_t>(cur, uw::kLutSize * 4);
     UW_HIP(hipMemcpy(h->d_lut_codes, lutc.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
     h->words_total = f.words.size();

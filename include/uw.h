@@ -142,8 +142,8 @@ uw_status uw_matmul(uw_handle h, const uint16_t* x_dev, float* y_dev, int64_t to
  * Scratch contents: pipeline 1, W as row-major bf16; pipelines 2 and 3, the
  * exponent bytes (16 per run) or 4-bit codes (8 bytes per run) of the serial
  * order regrouped: with chunk c = 256 serial weights (16 runs of 16) and run r
- * of it, the run sits at run slot (c/64 * 16 + r) * 64 + c%64 (whole groups of
- * 64 chunks, uw_info.scratch_bytes). */
+ * of it, the run sits at run slot (c/512 * 16 + r) * 512 + c%512 (whole groups
+ * of 512 chunks, uw_info.scratch_bytes). */
 uw_status uw_preprocess(uw_handle h, int pipeline);
 
 /* Streams (hipStream_t passed as void*; NULL = the null stream).  The side

@@ -79,11 +79,11 @@ def test_decode_bit_exact(env, name):
 
 def _serial_from_interleaved(buf, n, run_bytes):
     """Undo the scratch order of pipelines 2/3 (as the header states it): run
-    r of chunk c (256 weights, 16 runs) sits at run slot (c//64*16 + r)*64 + c%64."""
+    r of chunk c (256 weights, 16 runs) sits at run slot (c//512*16 + r)*512 + c%512."""
     chunks = n // 256
     c = np.arange(chunks)[:, None]
     r = np.arange(16)[None, :]
-    slot = (c // 64 * 16 + r) * 64 + c % 64            # [chunk, run]
+    slot = (c // 512 * 16 + r) * 512 + c % 512        # [chunk, run]
     runs = buf.reshape(-1, run_bytes)
     return runs[slot.reshape(-1)].reshape(-1)[: n * run_bytes // 16]
 
