@@ -227,7 +227,9 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
     xs = synth.activations(max(tokens_list), hidden, xseed=1)
     for tokens in tokens_list:
         x = uw.bf16_tensor(xs[:tokens])
-        res = tune_split(torch, stack, pipes_easy_hard, x, tokens, [0, 32, 64, 128], steps=steps, log=log)
+        # side-stream CU counts; all CUs = both streams share every CU
+        res = tune_split(torch, stack, pipes_easy_hard, x, tokens, [0, 32, 64, 128, uw.device_cu_count()],
+                         steps=steps, log=log)
         best_ms, best_split = res[0]
         serial = [ms for ms, n in res if n == 0][0]
         # all layers read as direct palette would need palette copies of the hard layers; time instead the

@@ -86,11 +86,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
       const int kb = kb0 + u * WAVES;
       if (kb >= hi) break;
       const uint32_t b = (uint32_t)brick_row0 + kb;
-      st.s[u] = ld16(rs_sm, lane16, b * 1024);
+      st.s[u] = ld16s(rs_sm, lane16, b * 1024);
       if (EXPM) {
-        st.e[u] = ld16(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
+        st.e[u] = ld16s(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
       } else {
-        st.n[u] = ld8(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
+        st.n[u] = ld8s(rs_codes, clane, code_brick_off(b, CS, codes_ilv));
         const uint32_t map = mnext[u].x;
         st.anyraw[u] = map;
         st.raw[u] = (map >> r) & 1u;
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     const uint32_t map = __builtin_amdgcn_readfirstlane(m.x);
     const uint32_t before = __builtin_amdgcn_readfirstlane(m.y);
     const uint32_t b = brick_row0 + kb;
-    st.s = ld16(rs_sm, lane16, b * 1024);
-    st.n = ld8(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
+    st.s = ld16s(rs_sm, lane16, b * 1024);
+    st.n = ld8s(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
     st.map = map;
     const bool raw = (map >> r) & 1u;
     const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));

@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
 #pragma unroll
     for (int k = 0; k < SV; ++k) {
       const uint32_t i = threadIdx.x + k * kThreads;
-      sv[k] = ld16(rs_words, i < nvec ? (a0 + 4 * i) * 4 : kOffRange, 0);
+      sv[k] = ld16s(rs_words, i < nvec ? (a0 + 4 * i) * 4 : kOffRange, 0);
     }
 #pragma unroll
     for (int k = 0; k < LV; ++k) ((u32x4*)lut)[threadIdx.x + k * kThreads] = lv[k];
