@@ -26,10 +26,10 @@ struct FusedW {
 // `ksplit` workgroups (atomic accumulation into a zeroed Y).  Large-batch
 // kernels (tokens > 64): see fused_large.hip.
 struct Variant {
-  int kind;    // 0 = small batch, 1 = large batch
-  int waves;   // small: waves per workgroup
+  int kind;    // 0 = small batch, 1 = large batch, 2 = gemv (x in LDS), 3 = mid (K slices of x in LDS)
+  int waves;   // small/gemv/mid: waves per workgroup
   int ksplit;  // small: workgroups along K
-  int unroll;  // small: bricks in flight per wave
+  int unroll;  // small: bricks in flight per wave; gemv/mid: ring depth
   int tile;    // large: tile shape id
 };
 int variant_count(int64_t tokens);
@@ -42,6 +42,13 @@ Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_m
 // bf16 and at most kGemvKbnMax 64-column bricks per row.
 constexpr int64_t kGemvXElems = 16384;
 constexpr int64_t kGemvKbnMax = 1024;
+// LDS budget of the mid kernels (a K slice of the activations plus the
+// per-brick tables, or the epilogue's partial sums): two workgroups per CU.
+constexpr size_t kMidLdsBytes = 81920;
+// Bricks per K slice of the mid kernels for `tokens` tokens and `waves`
+// brick-rows per workgroup, and its LDS bytes.
+int mid_slice_kb(int64_t tokens, int64_t rows, int64_t cols, int waves);
+size_t mid_lds_bytes(int64_t tokens, int waves, int slice_kb);
 const char* variant_name(int64_t tokens, int id);
 // Name of a variant (its list entry, else a description of its fields).
 void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len);

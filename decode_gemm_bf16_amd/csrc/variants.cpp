@@ -15,6 +15,8 @@ hipError_t launch_fused_large(const FusedW& w, const uint16_t* x, float* y, int6
                               hipStream_t s);
 hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                              hipStream_t s);
+hipError_t launch_fused_mid(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                            hipStream_t s);
 
 namespace {
 
@@ -34,6 +36,9 @@ const Named kSmall[] = {
     // x held in LDS (palette forms, tokens x cols <= 16384); {waves, ring depth}
     {{2, 8, 1, 2, 0}, "gemv:w8:d2"},      {{2, 16, 1, 2, 0}, "gemv:w16:d2"},
     {{2, 8, 1, 3, 0}, "gemv:w8:d3"},      {{2, 4, 1, 3, 0}, "gemv:w4:d3"},
+    // a K slice of x in LDS shared by `waves` brick-rows; {waves, ring depth}
+    {{3, 16, 1, 2, 0}, "mid:w16:d2"},     {{3, 8, 1, 2, 0}, "mid:w8:d2"},
+    {{3, 16, 1, 3, 0}, "mid:w16:d3"},     {{3, 4, 1, 2, 0}, "mid:w4:d2"},
 };
 // large batch: kind 1, {tile, ksplit}
 const Named kLarge[] = {
@@ -89,6 +94,8 @@ void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len) {
     snprintf(buf, len, "large:t%d:k%d", v.tile, v.ksplit);
   else if (v.kind == 2)
     snprintf(buf, len, "gemv:w%d:d%d", v.waves, v.unroll);
+  else if (v.kind == 3)
+    snprintf(buf, len, "mid:w%d:d%d", v.waves, v.unroll);
   else
     snprintf(buf, len, "small:w%d:k%d:u%d", v.waves, v.ksplit, v.unroll);
 }
@@ -115,6 +122,9 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
     if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128) return Variant{2, 8, 1, 2, 0};
+    // from 16 tokens: K slices of the activations in LDS shared by 8
+    // brick-rows (the small kernel reads them from L2 once per brick-row)
+    if (tokens >= 16) return Variant{3, 8, 1, 2, 0};
     return small_default(tokens, rows, cols);
   }
   // 256 x 256 tiles with the rebuild interleaved into the MFMAs once there are
@@ -150,6 +160,7 @@ hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t to
   const Variant v = variant_effective(tokens, w.rows, w.cols, w.exp_mode, v0);
   if (tokens <= 64) {
     if (v.kind == 2) return launch_fused_gemv(w, x, y, tokens, v, s);
+    if (v.kind == 3) return launch_fused_mid(w, x, y, tokens, v, s);
     if (v.kind != 0) return hipErrorInvalidValue;
     return launch_fused_small(w, x, y, tokens, v, s);
   }

@@ -129,7 +129,7 @@ def test_matmul_random_all_pipelines(env, shape, tokens):
         assert oracle.rel_err(y, ref) <= TOL, (p, oracle.rel_err(y, ref))
 
 
-@pytest.mark.parametrize("tokens", [1, 16, 64, 100, 256])
+@pytest.mark.parametrize("tokens", [1, 16, 40, 64, 100, 256])
 def test_every_variant(env, tokens):
     torch, uw = env
     w = synth.weights(528, 1024, 2, 0.002, 12)
