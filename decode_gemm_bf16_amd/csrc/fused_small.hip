@@ -242,7 +242,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     st.map = map;
     const bool raw = (map >> r) & 1u;
     const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-    st.e = ld16s(rs_side, raw ? (before + rank) * 64 + q * 16 : kOffRange, 0);
+    st.e = ld16(rs_side, raw ? (before + rank) * 64 + q * 16 : kOffRange, 0);
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const GStage& st, int i) {
