@@ -227,7 +227,9 @@ int resolve_pipeline(const uw_matrix* h, int64_t tokens, int pipeline, int* vari
   if (pipeline != UW_P_AUTO) return pipeline;
   for (int i = 0; i < h->plan_n; ++i)
     if (tokens <= h->plan_tok[i]) {
-      *variant = h->plan_var[i];
+      // a variant id names a kernel of its batch family (<= 64 tokens or
+      // more): an entry tuned in the other family keeps only its pipeline
+      *variant = (tokens <= 64) == (h->plan_tok[i] <= 64) ? h->plan_var[i] : 0;
       return h->plan_pipe[i];
     }
   *variant = 0;

@@ -59,6 +59,10 @@ const Named kLarge[] = {
     {{1, 0, 2, 0, 10}, "large:t10(4x64r x256t,32x32,interleaved):k2"},
     {{1, 0, 1, 0, 11}, "large:t11(4x64r x256t,32x32,interleaved,B groups):k1"},
     {{1, 0, 2, 0, 11}, "large:t11(4x64r x256t,32x32,interleaved,B groups):k2"},
+    // weights requested D steps ahead into registers, activations X-1 steps ahead straight to LDS
+    {{1, 0, 1, 0, 12}, "large:t12(4x32r x128t,32x32,ring d4 x3)"},
+    {{1, 0, 1, 0, 13}, "large:t13(4x32r x64t,32x32,ring d4 x3)"},
+    {{1, 0, 1, 0, 14}, "large:t14(4x64r x128t,32x32,ring d3 x3)"},
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -131,6 +135,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   // enough tokens to fill the chip with them (one workgroup per CU)
   const int64_t wg11 = ((brows + 15) / 16) * ((tokens + 255) / 256);
   if (tokens >= 512 && wg11 >= 192) return Variant{1, 0, 1, 0, 11};
+  // below that, the deep-prefetch tiles (128 rows) where they fill the chip
+  const int64_t rb8 = (brows + 7) / 8;
+  if (tokens <= 192 && rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, 13};
+  if (rb8 * ((tokens + 127) / 128) >= 192) return Variant{1, 0, 1, 0, 12};
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
   const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tiles 1/5: 128 rows per workgroup

@@ -158,7 +158,10 @@ uw_status uw_set_scratch(uw_handle h, void* scratch_dev, size_t bytes);
 
 /* Autotuner output (section 九): for UW_P_AUTO, the first entry with
  * tokens <= max_tokens[i] selects pipeline[i] and kernel variant[i]
- * (variant 0 = built-in choice).  n <= 16; n = 0 clears the plan. */
+ * (variant 0 = built-in choice).  Variant ids name kernels of one batch
+ * family (tokens <= 64, or more; see uw_variant_name): an entry whose
+ * max_tokens lies in the other family than the call's token count applies
+ * its pipeline with the built-in variant.  n <= 16; n = 0 clears the plan. */
 uw_status uw_set_plan(uw_handle h, const int32_t* max_tokens, const int32_t* pipeline,
                       const int32_t* variant, int32_t n);
 

@@ -149,9 +149,15 @@ def test_variant_in_use_resolution():
     assert m.variant_in_use(1, uw.P4_DIRECT_PALETTE) == (uw.P4_DIRECT_PALETTE, "small:w8:k1:u2")
     m.set_variant(0)
     # a plan selects pipeline and variant per batch size
-    m.set_plan([(16, uw.P1_FULL_DECODE, 0), (1 << 30, uw.P4_DIRECT_PALETTE, v)])
+    vl = uw.variants(100).index("large:t5(4x32r x128t,32x32):k1")
+    m.set_plan([(16, uw.P1_FULL_DECODE, 0), (64, uw.P4_DIRECT_PALETTE, v), (1 << 30, uw.P4_DIRECT_PALETTE, vl)])
     assert m.variant_in_use(1) == (uw.P1_FULL_DECODE, "hipblaslt")
     assert m.variant_in_use(17) == (uw.P4_DIRECT_PALETTE, "small:w8:k1:u2")
+    assert m.variant_in_use(100) == (uw.P4_DIRECT_PALETTE, "large:t5(4x32r x128t,32x32):k1")
+    # a variant id names a kernel of its batch family (<= 64 tokens or more):
+    # an entry tuned above 64 tokens keeps only its pipeline for 17 tokens
+    m.set_plan([(1 << 30, uw.P4_DIRECT_PALETTE, vl)])
+    assert m.variant_in_use(17) == m.variant_in_use(17, uw.P4_DIRECT_PALETTE)
     with pytest.raises(uw.UwError) as e:
         uw.Matrix(synth.weights(64, 64, 1, 0.0, 0), uw.FMT_PALETTE | uw.ENC_HOST_ONLY).variant_in_use(1, uw.P1_FULL_DECODE)
     assert e.value.status in (uw.ERR_UNSUPPORTED, uw.ERR_INVALID_ARG)
