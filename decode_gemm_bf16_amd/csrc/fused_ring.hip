@@ -22,8 +22,8 @@
 //  * the per-brick tables of the workgroup's brick-rows are copied to LDS
 //    once, so no scalar load sits on a step's critical path.
 // Tiles in LDS have no padding (the DMA writes 1 KB runs); the 16-byte piece
-// p of token t sits at piece p ^ (t & 7) of its 128-byte row instead, which
-// spreads a B fragment's 32 tokens over the banks.
+// p of token t sits at piece p ^ ((t/2) & 7) of its 128-byte row instead,
+// which spreads a B fragment's 32 tokens over the banks.
 #include "kernels.h"
 #include "recon.h"
 
@@ -109,13 +109,13 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
     voff_s[rb] = row_ok[rb] ? run * 16 + (uint32_t)pb * kbn * 1024 : kOffRange;
   }
   // activation DMA: load j of this wave moves chunk c = j*WAVES + wave (8
-  // tokens x 128 bytes); lane i carries token 8c + i/8, stored piece i%8,
-  // which holds global piece (i%8) ^ ((i/8) & 7)
+  // tokens x 128 bytes); lane i carries token t = 8c + i/8, stored piece i%8,
+  // which holds global piece (i%8) ^ ((t/2) & 7)
   uint32_t xoff[XL];
 #pragma unroll
   for (int j = 0; j < XL; ++j) {
     const int c = j * WAVES + wave, t = c * 8 + (lane >> 3);
-    const int p = (lane & 7) ^ ((lane >> 3) & 7);
+    const int p = (lane & 7) ^ ((t >> 1) & 7);
     xoff[j] = tok0 + t < tokens ? ((uint32_t)(tok0 + t) * cols + p * 8) * 2 : kOffRange;
   }
   auto issue_x = [&](int kb) {
@@ -128,12 +128,15 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
     }
   };
   // B fragment offsets: token lane%32 of a 32-token block, piece p(ph) =
-  // 2*ks2 + 4*(ph/2) + ph%2 for the (K pair, half) group ph
+  // 2*ks2 + 4*(ph/2) + ph%2 for the (K pair, half) group ph.  With the swizzle
+  // by (token/2) % 8 the 64 lanes of a read (32 tokens, two pieces) fall four
+  // to each 16-byte bank group of a 256-byte bank row: no conflicts beyond
+  // the four passes 1 KB needs.
   uint32_t bsw[4];
 #pragma unroll
   for (int ph = 0; ph < 4; ++ph) {
     const int p = 2 * ks2 + 4 * (ph >> 1) + (ph & 1);
-    bsw[ph] = (uint32_t)(lane & 31) * 128 + (uint32_t)((p ^ (lane & 7)) * 16);
+    bsw[ph] = (uint32_t)(lane & 31) * 128 + (uint32_t)((p ^ (((lane & 31) >> 1) & 7)) * 16);
   }
 
   auto table = [&](int i, int b2, int kb, bool in_lds) -> uint2 {
@@ -141,21 +144,29 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
     if (EXPM || br >= brows) return uint2{0u, 0u};
     return in_lds ? mtab[(br - wbr0) * kbn + kb] : meta[(size_t)br * kbn + kb];
   };
+  // code loads: a per-lane part (run, and out of range for absent rows), the
+  // brick's wave-uniform part as the scalar offset, and for the second brick
+  // of the pair the (uniform) difference of the two
+  constexpr uint32_t CS = EXPM ? 16 : 8;
+  uint32_t clo[RB2][2];
+#pragma unroll
+  for (int i = 0; i < RB2; ++i)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) clo[i][p] = row_ok[i] ? code_lane_off(2 * p + ks2, r, CS, codes_ilv) : kOffRange;
   auto load_w = [&](RStage<RB2, EXPM>& w, int kb, bool in_lds) {
     kb = min(kb, kbn - 1);  // past the end: re-read the last step (never used)
 #pragma unroll
     for (int i = 0; i < RB2; ++i) {
       const uint32_t b = (uint32_t)(brow0 + 2 * i) * kbn + kb;  // first brick of the pair
+      const uint32_t cb0 = code_brick_off(b, CS, codes_ilv), cb1 = code_brick_off(b + kbn, CS, codes_ilv);
+      const uint32_t dpb = pb ? cb1 - cb0 : 0u;
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         w.s[i][p] = ld16(rs_sm, voff_s[i], b * 1024 + p * 512);
-        const uint32_t co = row_ok[i] ? 0u : kOffRange;
         if (EXPM)
-          w.e[i][p] = ld16(rs_codes, co | (code_brick_off(b + (uint32_t)pb * kbn, 16, codes_ilv) +
-                                           code_lane_off(2 * p + ks2, r, 16, codes_ilv)), 0);
+          w.e[i][p] = ld16(rs_codes, clo[i][p] + dpb, cb0);
         else
-          w.n[i][p] = ld8(rs_codes, co | (code_brick_off(b + (uint32_t)pb * kbn, 8, codes_ilv) +
-                                          code_lane_off(2 * p + ks2, r, 8, codes_ilv)), 0);
+          w.n[i][p] = ld8(rs_codes, clo[i][p] + dpb, cb0);
       }
       if (!EXPM) {
         const uint2 ma = table(i, 0, kb, in_lds), mb = table(i, 1, kb, in_lds);
@@ -195,9 +206,10 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
   __builtin_amdgcn_s_waitcnt(0);  // every load of the prologue (the first tile included)
   __syncthreads();
 
-  auto step = [&](RStage<RB2, EXPM>& ws, int kb) {
-    // A fragments of step kb
-    bf16x8 a[RB2][2][2];
+  // A fragments of a step: the branch-free rebuild (palette rows; the
+  // exponent form is all of it), then the rows of raw groups (rare, a
+  // wave-uniform branch)
+  auto rebuild = [&](const RStage<RB2, EXPM>& ws, bf16x8 (&an)[RB2][2][2]) {
 #pragma unroll
     for (int i = 0; i < RB2; ++i)
 #pragma unroll
@@ -208,23 +220,42 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
         } else {
           uint32_t v[4];
           palette_v(ws.n[i][p], lut, v);
-          if (ws.anyraw[i]) {
-            if (ws.raw[i]) {
-              v[0] = rot_exp(ws.e[i][p].x);
-              v[1] = rot_exp(ws.e[i][p].y);
-              v[2] = rot_exp(ws.e[i][p].z);
-              v[3] = rot_exp(ws.e[i][p].w);
-            }
-          }
           rebuild_v2(ws.s[i][p], v, a0, a1);
         }
-        a[i][p][0] = as_bf16x8(a0);
-        a[i][p][1] = as_bf16x8(a1);
+        an[i][p][0] = as_bf16x8(a0);
+        an[i][p][1] = as_bf16x8(a1);
       }
-    // requests: weights of step kb+D into the freed stage, tile of step kb+X-1
-    load_w(ws, kb + D, true);
+  };
+  auto patch_raw = [&](const RStage<RB2, EXPM>& ws, bf16x8 (&an)[RB2][2][2]) {
+    if (EXPM) return;
+#pragma unroll
+    for (int i = 0; i < RB2; ++i)
+      if (ws.anyraw[i]) {
+        if (ws.raw[i]) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            u32x4 a0, a1;
+            rebuild_exp2(ws.s[i][p], ws.e[i][p], a0, a1);
+            an[i][p][0] = as_bf16x8(a0);
+            an[i][p][1] = as_bf16x8(a1);
+          }
+        }
+      }
+  };
+
+  bf16x8 a[2][RB2][2][2];
+  rebuild(w[0], a[0]);
+  patch_raw(w[0], a[0]);
+  // One step: request the weights of step kb+D (into the stage step kb was
+  // rebuilt from) and the tile of step kb+X-1; the MFMAs of step kb on a[C],
+  // each followed by a few VALU ops of the rebuild of step kb+1 into a[C^1]
+  // (one wave per SIMD: the VALU issues while the matrix core works); then
+  // the raw rows of step kb+1, the wait for this wave's part of tile kb+1
+  // and the barrier that publishes it.
+  auto step = [&](RStage<RB2, EXPM>& wcur, const RStage<RB2, EXPM>& wnext, bf16x8 (&ac)[RB2][2][2],
+                  bf16x8 (&an)[RB2][2][2], int kb) {
+    load_w(wcur, kb + D, true);
     issue_x(kb + X - 1);
-    // MFMAs on tile kb: 4 (K pair, half) groups x TB2 token blocks x RB2 row pairs
     const uint8_t* xb = ring_lds + (kb % X) * TILE;
     u32x4 bf[2];
     bf[0] = *(const u32x4*)(xb + bsw[0]);
@@ -238,22 +269,32 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
       const bf16x8 bv = as_bf16x8(bf[jj & 1]);
 #pragma unroll
       for (int i = 0; i < RB2; ++i)
-        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][ph >> 1][ph & 1], bv, acc[i][t], 0, 0, 0);
+        acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i][ph >> 1][ph & 1], bv, acc[i][t], 0, 0, 0);
     }
+    rebuild(wnext, an);
+#pragma unroll
+    for (int jj = 0; jj < 4 * TB2 * RB2; ++jj) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // then up to six VALU ops
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // and an LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    patch_raw(wnext, an);
     // this wave's part of tile kb+1 (requested X-2 steps ago) has landed once
     // at most the loads of the X-2 later steps are outstanding
     wait_vmcnt<(X - 2) * (WL + XL)>();
     __syncthreads();
   };
 
+  static_assert(D % 2 == 0, "the A fragments alternate with the ring stage");
   int kb = 0;
   for (; kb + D <= kbn; kb += D) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) step(w[j], kb + j);
+    for (int j = 0; j < D; ++j) step(w[j], w[(j + 1) % D], a[j & 1], a[(j + 1) & 1], kb + j);
   }
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (kb + j < kbn) step(w[j], kb + j);
+    if (kb + j < kbn) step(w[j], w[(j + 1) % D], a[j & 1], a[(j + 1) & 1], kb + j);
 
 #pragma unroll
   for (int i = 0; i < RB2; ++i) {
@@ -297,12 +338,16 @@ hipError_t launch_ring_t(const FusedW& w, const uint16_t* x, float* y, int64_t t
 }  // namespace
 
 // tile ids 12..: 12 = 4 waves x (32 rows x 128 tokens), D 4, X 3; 13 = 4 waves x
-// (32 rows x 64 tokens), D 4, X 3; 14 = 4 waves x (64 rows x 128 tokens), D 3, X 3
+// (32 rows x 64 tokens), D 4, X 3; 14 = 4 waves x (64 rows x 128 tokens), D 2, X 3;
+// 15 = 12 with X 8; 16 = 13 with X 8; 17 = 12 with D 6, X 6
 hipError_t launch_fused_ring(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int tile, hipStream_t s) {
   switch (tile) {
     case 12: return launch_ring_t<1, 4, 4, 3>(w, x, y, tokens, s);
     case 13: return launch_ring_t<1, 2, 4, 3>(w, x, y, tokens, s);
-    case 14: return launch_ring_t<2, 4, 3, 3>(w, x, y, tokens, s);
+    case 14: return launch_ring_t<2, 4, 2, 3>(w, x, y, tokens, s);
+    case 15: return launch_ring_t<1, 4, 4, 8>(w, x, y, tokens, s);
+    case 16: return launch_ring_t<1, 2, 4, 8>(w, x, y, tokens, s);
+    case 17: return launch_ring_t<1, 4, 6, 6>(w, x, y, tokens, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -62,7 +62,10 @@ const Named kLarge[] = {
     // weights requested D steps ahead into registers, activations X-1 steps ahead straight to LDS
     {{1, 0, 1, 0, 12}, "large:t12(4x32r x128t,32x32,ring d4 x3)"},
     {{1, 0, 1, 0, 13}, "large:t13(4x32r x64t,32x32,ring d4 x3)"},
-    {{1, 0, 1, 0, 14}, "large:t14(4x64r x128t,32x32,ring d3 x3)"},
+    {{1, 0, 1, 0, 14}, "large:t14(4x64r x128t,32x32,ring d2 x3)"},
+    {{1, 0, 1, 0, 15}, "large:t15(4x32r x128t,32x32,ring d4 x8)"},
+    {{1, 0, 1, 0, 16}, "large:t16(4x32r x64t,32x32,ring d4 x8)"},
+    {{1, 0, 1, 0, 17}, "large:t17(4x32r x128t,32x32,ring d6 x6)"},
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -137,8 +140,7 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   if (tokens >= 512 && wg11 >= 192) return Variant{1, 0, 1, 0, 11};
   // below that, the deep-prefetch tiles (128 rows) where they fill the chip
   const int64_t rb8 = (brows + 7) / 8;
-  if (tokens <= 192 && rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, 13};
-  if (rb8 * ((tokens + 127) / 128) >= 192) return Variant{1, 0, 1, 0, 12};
+  if (rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, tokens <= 192 ? 13 : 16};
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
   const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tiles 1/5: 128 rows per workgroup
