@@ -143,6 +143,27 @@ def test_every_variant(env, tokens):
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p)
 
 
+@pytest.mark.parametrize("tokens", [17, 40, 64, 100, 200])
+def test_ragged_k_slices_and_ring_tails(env, tokens):
+    """K of 27 bricks (1728 columns), 34 brick-rows: the mid kernels split K
+    into slices of unequal length (float atomics into a zeroed Y), the ring
+    tiles run a step count that is not a multiple of their register ring and
+    a last row block with absent brick-rows; every variant, both the exponent
+    form (pipeline 2, interleaved scratch) and the direct palette form."""
+    torch, uw = env
+    w = synth.weights(544, 1728, 5, 0.003, 11)
+    x = synth.activations(tokens, 1728, xseed=7)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    names = uw.variants(tokens)
+    picked = [v for v, n in enumerate(names) if n.startswith(("mid", "large:t1", "small:default", "large:default"))]
+    assert picked
+    for v in picked:
+        for p in (2, 4):
+            y = _run(env, m, x, p, variant=v)
+            assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
+
+
 def test_gate_full_size_batch1(env):
     """14336x4096 gate, batch 1 (the headline workload): full decode bit-exact,
     resident codes bit-exact, sampled outputs of all pipelines vs fp64."""
