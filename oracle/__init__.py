@@ -32,6 +32,7 @@ from .huffman import (  # noqa: F401
     huffman_lengths, canonical_codes, huffman_encode, huffman_decode,
     huffman_decode_chunks, huffman_bits_per_weight, kraft_sum,
 )
+from .bundle import read_bundle, write_bundle, transcode_bundle  # noqa: F401
 from .gemm import (  # noqa: F401
     bf16_to_f64, f64_to_bf16_rne, matmul_fp64, matmul_fp64_rows, silu_mul_bf16,
     mlp_layer_fp64, rel_err,
@@ -51,4 +52,7 @@ PARITY = {
     "huffman_encode/decode": "bit-exact round trip; hand-worked bitstream fixture",
     "matmul_fp64": "exact rational (Fraction) sums on the tiny case; one-hot identity",
     "silu_mul_bf16": "closed-form values; RNE ties by hand",
+    "write_bundle/read_bundle": "round trip to the original weights; byte-equal to the library's own writer "
+                                "(an independent implementation of the same layout); header fields by struct",
+    "transcode_bundle": "equals palette_encode of the original weights (the Huffman round trip is exact)",
 }
