@@ -262,6 +262,35 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
     return out
 
 
+def bundle_load_bench(uw, w, reps: int = 3) -> dict:
+    """The gate's Huffman form written to a bundle file, then loaded straight
+    into the direct-palette form (the exponents decoded and transcoded to 4-bit
+    codes and raw-group tables on the device).  Wall-clock seconds, file read
+    included; the kernels' own durations come from a kernel trace."""
+    import tempfile
+    m = uw.Matrix(w, uw.FMT_HUFFMAN)
+    d = tempfile.mkdtemp(prefix="uwbundle")
+    path = os.path.join(d, "gate.uwb")
+    t0 = time.perf_counter()
+    m.save(path)
+    save_s = time.perf_counter() - t0
+    m.free()
+    size = os.path.getsize(path)
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        lm = uw.Matrix.load(path, uw.FMT_PALETTE)
+        times.append(time.perf_counter() - t0)
+        info = lm.info()
+        lm.free()
+    os.remove(path)
+    os.rmdir(d)
+    log(f"bundle: {size / 1e6:.1f} MB, save {save_s:.3f} s, load+transcode {min(times):.3f} s")
+    return {"bundle_bytes": size, "bf16_bytes": 2 * w.size, "bundle_bits_per_weight": round(8 * size / w.size, 4),
+            "save_s": round(save_s, 4), "load_palette_s": round(min(times), 4),
+            "palette_bits_per_weight": round(info["bpw_palette"], 4), "raw_groups": info["raw_groups"]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,6 +304,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
+    ap.add_argument("--load", action="store_true",
+                    help="also time a bundle file of the gate loaded into the palette form (device transcode)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -410,6 +441,8 @@ def main() -> int:
             for m in v:
                 m.free()
         torch.cuda.empty_cache()
+    if args.load:
+        result["bundle_load"] = bundle_load_bench(uw, w)
     if args.stack:
         for m in mats:
             m.free()

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libuw.so")
 
 # enums and flags of uw.h
 OK = 0
-ERR_INVALID_ARG, ERR_SHAPE, ERR_OOM, ERR_HIP, ERR_FORMAT, ERR_UNSUPPORTED, ERR_NO_DEVICE = 1, 2, 3, 4, 5, 6, 7
+ERR_INVALID_ARG, ERR_SHAPE, ERR_OOM, ERR_HIP, ERR_FORMAT, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_IO = 1, 2, 3, 4, 5, 6, 7, 8
 P_AUTO, P1_FULL_DECODE, P2_EXP_DECODE, P3_PALETTE_TRANSCODE, P4_DIRECT_PALETTE = 0, 1, 2, 3, 4
 FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 (STREAM_SM, STREAM_NIBBLES, STREAM_RAWMAP, STREAM_RAWBEFORE, STREAM_SIDE, STREAM_WORDS, STREAM_OFFSETS,
@@ -26,7 +26,7 @@ FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 
 EXPORTED = [
     "uw_encode", "uw_decode", "uw_matmul", "uw_preprocess", "uw_set_streams", "uw_set_scratch", "uw_set_plan",
-    "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_free", "uw_last_error", "uw_silu_mul",
+    "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_save", "uw_load", "uw_free", "uw_last_error", "uw_silu_mul",
     "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_stack_forward", "uw_stack_workspace_bytes",
     "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy", "uw_device_read",
 ]
@@ -84,6 +84,8 @@ def _load() -> C.CDLL:
         "uw_query": ([vp, C.POINTER(Info)], st),
         "uw_export": ([vp, C.c_int, vp, C.c_size_t, C.POINTER(C.c_size_t)], st),
         "uw_clone": ([vp, C.POINTER(vp)], st),
+        "uw_save": ([vp, C.c_char_p], st),
+        "uw_load": ([C.c_char_p, u32, C.POINTER(vp)], st),
         "uw_free": ([vp], None),
         "uw_last_error": ([], C.c_char_p),
         "uw_silu_mul": ([vp, vp, vp, i64, vp], st),
@@ -182,6 +184,22 @@ class Matrix:
         _check(_lib.uw_clone(self._h, C.byref(h)))
         m = Matrix.__new__(Matrix)
         m._h, m.rows, m.cols, m.formats, m._keep = h, self.rows, self.cols, self.formats, []
+        return m
+
+    def save(self, path: str) -> None:
+        """Write the Huffman form to a bundle file (``uw_save``)."""
+        _check(_lib.uw_save(self._h, os.fsencode(path)))
+
+    @classmethod
+    def load(cls, path: str, formats: int = FMT_HUFFMAN | FMT_PALETTE) -> "Matrix":
+        """A matrix read from a bundle file; palette formats are transcoded on
+        the device (``uw_load``)."""
+        h = C.c_void_p()
+        _check(_lib.uw_load(os.fsencode(path), formats, C.byref(h)))
+        m = cls.__new__(cls)
+        m._h, m.formats, m._keep = h, formats, []
+        info = m.info()
+        m.rows, m.cols = info["rows"], info["cols"]
         return m
 
     def decode(self, out) -> None:

@@ -136,15 +136,8 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
 
   const bool want_pal = formats & (UW_FMT_PALETTE | UW_FMT_RAWAUX);
   if (want_pal) {
-    // Section 四: the 16 most frequent exponents, ties to the smaller value.
-    std::array<int, 256> order;
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return f.hist[a] > f.hist[b]; });
-    const int used = std::min<int>(16, int(f.distinct));
-    for (int i = 0; i < 16; ++i) f.palette[i] = uint8_t(order[i < used ? i : 0]);
-    std::array<int16_t, 256> code_of;
-    code_of.fill(-1);
-    for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = int16_t(i);
+    int16_t code_of[256];
+    select_palette(f.hist, f.palette, code_of);
 
     const uint64_t nb = f.bricks();
     f.rawmap.assign(nb, 0);
@@ -189,27 +182,9 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
   }
 
   if (formats & UW_FMT_HUFFMAN) {
-    limited_code_lengths(f.hist, kLmax, f.lengths);
-    // Canonical codes: (length, symbol) order, consecutive values per length.
-    std::array<int, 256> order;
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-      const int la = f.lengths[a] ? f.lengths[a] : 99, lb = f.lengths[b] ? f.lengths[b] : 99;
-      return la < lb;
-    });
-    uint32_t code = 0;
-    int prev_len = f.lengths[order[0]];
-    for (int i = 0; i < 256 && f.lengths[order[i]]; ++i) {
-      const int s = order[i];
-      code <<= (f.lengths[s] - prev_len);
-      prev_len = f.lengths[s];
-      f.codes[s] = code++;
-    }
-    uint64_t total = 0;
-    for (int s = 0; s < 256; ++s) total += f.hist[s] * f.lengths[s];
-    // bit positions are 32-bit on the device, look-ahead past the last code included
-    if (total >= (uint64_t(1) << 32) - 1024) return "Huffman stream longer than 2^32 - 1024 bits";
-    f.stream_bits = total;
+    std::string err = huffman_tables(f);
+    if (!err.empty()) return err;
+    const uint64_t total = f.stream_bits;
     const uint64_t payload = (total + 31) / 32;
     f.words.assign(payload + kStreamPadWords, 0);
     f.offsets.resize((n + kChunk - 1) / kChunk);
@@ -229,14 +204,55 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
       }
     }
     if (pending) f.words[wi++] = uint32_t(acc << (32 - pending));
-    // Decode table: every 12-bit window starting with a code maps to it.
-    f.lut.assign(kLutSize, 0);
-    for (int s = 0; s < 256; ++s) {
-      const int len = f.lengths[s];
-      if (!len) continue;
-      const uint32_t first = f.codes[s] << (kLmax - len), count = 1u << (kLmax - len);
-      for (uint32_t k = 0; k < count; ++k) f.lut[first + k] = uint16_t(s | (len << 8));
-    }
+  }
+  return std::string();
+}
+
+int select_palette(const uint64_t hist[256], uint8_t palette[16], int16_t code_of[256]) {
+  // Section 四: the 16 most frequent exponents, ties to the smaller value;
+  // with fewer than 16 distinct exponents the rest repeat entry 0
+  std::array<int, 256> order;
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return hist[a] > hist[b]; });
+  int distinct = 0;
+  for (int s = 0; s < 256; ++s) distinct += hist[s] != 0;
+  const int used = std::min(16, distinct);
+  for (int i = 0; i < 16; ++i) palette[i] = uint8_t(order[i < used ? i : 0]);
+  for (int s = 0; s < 256; ++s) code_of[s] = -1;
+  for (int i = used - 1; i >= 0; --i) code_of[palette[i]] = int16_t(i);
+  return used;
+}
+
+std::string huffman_tables(HostFormat& f) {
+  limited_code_lengths(f.hist, kLmax, f.lengths);
+  // Canonical codes: (length, symbol) order, consecutive values per length.
+  std::array<int, 256> order;
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    const int la = f.lengths[a] ? f.lengths[a] : 99, lb = f.lengths[b] ? f.lengths[b] : 99;
+    return la < lb;
+  });
+  std::memset(f.codes, 0, sizeof f.codes);
+  uint32_t code = 0;
+  int prev_len = f.lengths[order[0]];
+  for (int i = 0; i < 256 && f.lengths[order[i]]; ++i) {
+    const int s = order[i];
+    code <<= (f.lengths[s] - prev_len);
+    prev_len = f.lengths[s];
+    f.codes[s] = code++;
+  }
+  uint64_t total = 0;
+  for (int s = 0; s < 256; ++s) total += f.hist[s] * f.lengths[s];
+  // bit positions are 32-bit on the device, look-ahead past the last code included
+  if (total >= (uint64_t(1) << 32) - 1024) return "Huffman stream longer than 2^32 - 1024 bits";
+  f.stream_bits = total;
+  // Decode table: every 12-bit window starting with a code maps to it.
+  f.lut.assign(kLutSize, 0);
+  for (int s = 0; s < 256; ++s) {
+    const int len = f.lengths[s];
+    if (!len) continue;
+    const uint32_t first = f.codes[s] << (kLmax - len), count = 1u << (kLmax - len);
+    for (uint32_t k = 0; k < count; ++k) f.lut[first + k] = uint16_t(s | (len << 8));
   }
   return std::string();
 }

@@ -67,6 +67,16 @@ std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut);
 // bits 27-31 the bits they take.
 std::vector<uint32_t> multi_code_table(const std::vector<uint16_t>& lut, const uint8_t code_of[256]);
 
+// Section 四: the palette of a histogram (the 16 most frequent exponents, ties
+// to the smaller value, padded with entry 0) and code_of[e] = e's palette
+// index or -1.  Returns the number of distinct palette entries (<= 16).
+int select_palette(const uint64_t hist[256], uint8_t palette[16], int16_t code_of[256]);
+
+// The canonical code of f.hist: lengths, codes, stream_bits and the one-symbol
+// decode table (f.words and f.offsets are left alone).  Empty string on
+// success, else the reason.
+std::string huffman_tables(HostFormat& f);
+
 // Length-limited optimal code lengths over a 256-symbol histogram.
 void limited_code_lengths(const uint64_t hist[256], int lmax, uint8_t lengths[256]);
 

@@ -20,6 +20,7 @@
 #include "../../include/uw.h"
 #include "codec.h"
 #include "kernels.h"
+#include "transcode.h"
 
 namespace {
 
@@ -325,14 +326,18 @@ T* carve(uint8_t*& cur, size_t bytes) {
   return p;
 }
 
-uw_status upload(uw_matrix* h) {
+// Allocate the handle's device memory and copy the host streams into it.
+// With device_tables (load-time transcode) the palette tables, codes
+// included, are left for the caller's kernels to write.
+uw_status upload(uw_matrix* h, bool device_tables = false) {
   const uw::HostFormat& f = h->hf;
   const uint64_t n = f.n();
   const uint64_t nb = f.bricks();
   size_t total = align256(n);  // sm
   const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
+  const size_t side_bytes = std::max<size_t>(f.n_raw * 64, 64);
   if (pal) total += align256(n / 2);
-  if (tabs || huf) total += align256(nb * 8) + align256(std::max<size_t>(f.side.size(), 64));
+  if (tabs || huf) total += align256(nb * 8) + align256(side_bytes);
   if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + 2 * align256(uw::kLutSize * 4);
   if (hipMalloc(&h->dmem, total) != hipSuccess) {
     h->dmem = nullptr;
@@ -344,17 +349,20 @@ uw_status upload(uw_matrix* h) {
   UW_HIP(hipMemcpy(h->d_sm, f.sm.data(), n, hipMemcpyHostToDevice));
   if (pal) {
     h->d_nib = carve<uint8_t>(cur, n / 2);
-    UW_HIP(hipMemcpy(h->d_nib, f.nib.data(), n / 2, hipMemcpyHostToDevice));
+    if (!device_tables) UW_HIP(hipMemcpy(h->d_nib, f.nib.data(), n / 2, hipMemcpyHostToDevice));
   }
   if (tabs || huf) {
-    // per-brick {raw map, raw groups before}; all zero for a Huffman-only matrix
-    std::vector<uint2> meta(nb, uint2{0, 0});
-    if (tabs)
-      for (uint64_t b = 0; b < nb; ++b) meta[b] = uint2{f.rawmap[b], f.rawbefore[b]};
     h->d_meta = carve<uint2>(cur, nb * 8);
-    UW_HIP(hipMemcpy(h->d_meta, meta.data(), nb * 8, hipMemcpyHostToDevice));
-    h->d_side = carve<uint8_t>(cur, std::max<size_t>(f.side.size(), 64));
-    if (!f.side.empty()) UW_HIP(hipMemcpy(h->d_side, f.side.data(), f.side.size(), hipMemcpyHostToDevice));
+    if (!device_tables) {
+      // per-brick {raw map, raw groups before}; all zero for a Huffman-only matrix
+      std::vector<uint2> meta(nb, uint2{0, 0});
+      if (tabs)
+        for (uint64_t b = 0; b < nb; ++b) meta[b] = uint2{f.rawmap[b], f.rawbefore[b]};
+      UW_HIP(hipMemcpy(h->d_meta, meta.data(), nb * 8, hipMemcpyHostToDevice));
+    }
+    h->d_side = carve<uint8_t>(cur, side_bytes);
+    if (!device_tables && !f.side.empty())
+      UW_HIP(hipMemcpy(h->d_side, f.side.data(), f.side.size(), hipMemcpyHostToDevice));
   }
   if (huf) {
     h->d_words = carve<uint32_t>(cur, f.words.size() * 4);
@@ -398,6 +406,160 @@ void release_host_streams(uw::HostFormat& f) {
   std::vector<uint32_t>().swap(f.rawmap);
   std::vector<uint32_t>().swap(f.rawbefore);
   std::vector<uint16_t>().swap(f.lut);
+}
+
+}  // namespace
+
+// ---- distribution bundle (section 十) and load-time transcode (section 六) ----
+
+namespace {
+
+// File layout, little-endian: a 64-byte header, the exponent histogram
+// (256 x u64), the chunk bit offsets (u32), the Huffman payload words (u32,
+// without the padding words) and the serial sign+mantissa bytes.
+struct BundleHeader {
+  char magic[8];          // "UWBUNDLE"
+  uint32_t version;       // 1
+  uint32_t header_bytes;  // 64
+  int64_t rows, cols;
+  uint64_t stream_bits;
+  uint32_t chunk, lmax;   // 256, 12
+  uint64_t words;         // payload words
+  uint64_t offsets;       // chunk offsets
+};
+static_assert(sizeof(BundleHeader) == 64, "bundle header layout");
+constexpr char kBundleMagic[8] = {'U', 'W', 'B', 'U', 'N', 'D', 'L', 'E'};
+
+struct FileCloser {
+  FILE* f;
+  ~FileCloser() {
+    if (f) fclose(f);
+  }
+};
+
+// Device buffers of the load-time transcode, freed on every exit path.
+struct DevTemp {
+  void* p = nullptr;
+  ~DevTemp() {
+    if (p) {
+      (void)hipDeviceSynchronize();
+      (void)hipFree(p);
+    }
+  }
+};
+
+// Build the palette tables (and codes, for UW_FMT_PALETTE) of a loaded
+// Huffman form on the device: decode the exponents, find the raw rows, count
+// them, then allocate the handle's memory and fill codes and side table.
+uw_status transcode_upload(uw_matrix* h) {
+  uw::HostFormat& f = h->hf;
+  const uint64_t nb = f.bricks();
+  int16_t code_of[256];
+  uw::select_palette(f.hist, f.palette, code_of);
+  uw::CodeOfTable cof;
+  for (int i = 0; i < 256; ++i) cof.c[i] = int8_t(code_of[i]);
+  const std::vector<uint32_t> lut3 = uw::multi_symbol_table(f.lut);
+
+  uint8_t* cur = nullptr;
+  const size_t exps_bytes = h->scratch_need(2);
+  const size_t tbytes = align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + align256(lut3.size() * 4) +
+                        align256(exps_bytes) + align256(nb * 4) + 2 * align256(uw::transcode_groups(nb) * 4) + 256;
+  DevTemp tmp;
+  if (hipMalloc(&tmp.p, tbytes) != hipSuccess) {
+    tmp.p = nullptr;
+    return fail(UW_ERR_OOM, "device allocation of %zu bytes for the transcode failed", tbytes);
+  }
+  cur = static_cast<uint8_t*>(tmp.p);
+  uw::HuffDev d{};
+  uint32_t* words = carve<uint32_t>(cur, f.words.size() * 4);
+  uint32_t* offsets = carve<uint32_t>(cur, f.offsets.size() * 4);
+  uint32_t* lut = carve<uint32_t>(cur, lut3.size() * 4);
+  uint8_t* exps = carve<uint8_t>(cur, exps_bytes);
+  uint32_t* rawmap = carve<uint32_t>(cur, nb * 4);
+  const uint64_t ng = uw::transcode_groups(nb);
+  uint32_t* wg_count = carve<uint32_t>(cur, ng * 4);
+  uint32_t* wg_before = carve<uint32_t>(cur, ng * 4);
+  uint32_t* total = carve<uint32_t>(cur, 4);
+  UW_HIP(hipMemcpy(words, f.words.data(), f.words.size() * 4, hipMemcpyHostToDevice));
+  UW_HIP(hipMemcpy(offsets, f.offsets.data(), f.offsets.size() * 4, hipMemcpyHostToDevice));
+  UW_HIP(hipMemcpy(lut, lut3.data(), lut3.size() * 4, hipMemcpyHostToDevice));
+  d.words = words;
+  d.offsets = offsets;
+  d.lut = lut;
+  d.total_bits = f.stream_bits;
+  d.rows = h->rows;
+  d.cols = h->cols;
+  UW_HIP(uw::launch_huff_decode(d, uw::EMIT_EXP, exps, nullptr));
+  UW_HIP(uw::launch_raw_rows(exps, nb, cof, rawmap, wg_count, nullptr));
+  UW_HIP(uw::launch_raw_scan(wg_count, ng, wg_before, total, nullptr));
+  uint32_t n_raw = 0;
+  UW_HIP(hipMemcpy(&n_raw, total, 4, hipMemcpyDeviceToHost));
+  f.n_raw = n_raw;
+  uw_status st = upload(h, true);
+  if (st != UW_OK) return st;
+  UW_HIP(uw::launch_palette_pack(exps, nb, cof, rawmap, wg_before, h->d_meta,
+                                 h->has(UW_FMT_PALETTE) ? h->d_nib : nullptr, h->d_side, nullptr));
+  UW_HIP(hipDeviceSynchronize());
+  return UW_OK;
+}
+
+uw_status load_impl(const char* path, uint32_t formats, uw_matrix* h) {
+  FileCloser fc{fopen(path, "rb")};
+  if (!fc.f) return fail(UW_ERR_IO, "cannot open %s", path);
+  auto read = [&](void* dst, size_t bytes) { return bytes == 0 || fread(dst, 1, bytes, fc.f) == bytes; };
+  BundleHeader hd;
+  if (!read(&hd, sizeof hd) || std::memcmp(hd.magic, kBundleMagic, 8) != 0)
+    return fail(UW_ERR_IO, "%s is not a weight bundle", path);
+  if (hd.version != 1 || hd.header_bytes != sizeof hd) return fail(UW_ERR_FORMAT, "bundle version %u unknown", hd.version);
+  if (hd.chunk != uint32_t(uw::kChunk) || hd.lmax != uint32_t(uw::kLmax))
+    return fail(UW_ERR_FORMAT, "bundle chunk %u / code limit %u differ from this library's", hd.chunk, hd.lmax);
+  if (hd.rows <= 0 || hd.cols <= 0 || hd.rows % 16 || hd.cols % 64 || hd.rows > (int64_t(1) << 31) ||
+      hd.cols > (int64_t(1) << 31) || hd.rows * hd.cols >= (int64_t(1) << 31))
+    return fail(UW_ERR_SHAPE, "bundle shape %lldx%lld not supported", (long long)hd.rows, (long long)hd.cols);
+  uw::HostFormat& f = h->hf;
+  f.rows = h->rows = hd.rows;
+  f.cols = h->cols = hd.cols;
+  const uint64_t n = f.n();
+  if (hd.offsets != (n + uw::kChunk - 1) / uw::kChunk || hd.words != (hd.stream_bits + 31) / 32)
+    return fail(UW_ERR_FORMAT, "bundle table sizes do not match its shape and stream length");
+  if (!read(f.hist, sizeof f.hist)) return fail(UW_ERR_IO, "%s: truncated histogram", path);
+  uint64_t sum = 0;
+  for (int s = 0; s < 256; ++s) {
+    sum += f.hist[s];
+    f.distinct += f.hist[s] != 0;
+  }
+  if (sum != n) return fail(UW_ERR_FORMAT, "bundle histogram counts %llu weights, shape holds %llu",
+                            (unsigned long long)sum, (unsigned long long)n);
+  // the code is rebuilt from the histogram exactly as the encoder built it
+  const std::string err = uw::huffman_tables(f);
+  if (!err.empty()) return fail(UW_ERR_FORMAT, "%s", err.c_str());
+  if (f.stream_bits != hd.stream_bits)
+    return fail(UW_ERR_FORMAT, "bundle stream holds %llu bits, its histogram's code gives %llu",
+                (unsigned long long)hd.stream_bits, (unsigned long long)f.stream_bits);
+  try {
+    f.offsets.resize(hd.offsets);
+    f.words.assign(hd.words + uw::kStreamPadWords, 0);
+    f.sm.resize(n);
+  } catch (const std::bad_alloc&) {
+    return fail(UW_ERR_OOM, "host allocation failed while reading %s", path);
+  }
+  if (!read(f.offsets.data(), hd.offsets * 4) || !read(f.words.data(), hd.words * 4) || !read(f.sm.data(), n))
+    return fail(UW_ERR_IO, "%s: truncated bundle", path);
+  char extra;
+  if (fread(&extra, 1, 1, fc.f) != 0) return fail(UW_ERR_FORMAT, "%s: bytes after the bundle", path);
+  if (f.offsets[0] != 0) return fail(UW_ERR_FORMAT, "first chunk offset is not 0");
+  for (uint64_t c = 1; c < hd.offsets; ++c)
+    if (f.offsets[c] < f.offsets[c - 1] || f.offsets[c] > f.stream_bits)
+      return fail(UW_ERR_FORMAT, "chunk offset %llu out of order", (unsigned long long)c);
+
+  h->formats = f.formats = formats & 0x7u;
+  if (h->host_only) return UW_OK;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(UW_ERR_NO_DEVICE, "no HIP device");
+  uw_status st = h->has_pal_tables() ? transcode_upload(h) : upload(h);
+  if (st != UW_OK) return st;
+  release_host_streams(h->hf);
+  return UW_OK;
 }
 
 }  // namespace
@@ -700,6 +862,78 @@ uw_status uw_clone(uw_handle h, uw_handle* out) {
     return fail(UW_ERR_HIP, "device copy failed");
   }
   *out = c;
+  return UW_OK;
+}
+
+uw_status uw_save(uw_handle h, const char* path) {
+  if (!h || !path) return fail(UW_ERR_INVALID_ARG, "null argument");
+  if (!h->has(UW_FMT_HUFFMAN)) return fail(UW_ERR_UNSUPPORTED, "a bundle holds the Huffman form; the handle has none");
+  const uw::HostFormat& f = h->hf;
+  const uint64_t n = f.n();
+  BundleHeader hd{};
+  std::memcpy(hd.magic, kBundleMagic, 8);
+  hd.version = 1;
+  hd.header_bytes = sizeof hd;
+  hd.rows = h->rows;
+  hd.cols = h->cols;
+  hd.stream_bits = f.stream_bits;
+  hd.chunk = uw::kChunk;
+  hd.lmax = uw::kLmax;
+  hd.words = (f.stream_bits + 31) / 32;
+  hd.offsets = (n + uw::kChunk - 1) / uw::kChunk;
+  std::vector<uint32_t> words, offsets;
+  std::vector<uint8_t> sm;
+  const uint32_t* pw = f.words.data();
+  const uint32_t* po = f.offsets.data();
+  const uint8_t* ps = f.sm.data();
+  if (!h->host_only) {
+    try {
+      words.resize(hd.words);
+      offsets.resize(hd.offsets);
+      sm.resize(n);
+    } catch (const std::bad_alloc&) {
+      return fail(UW_ERR_OOM, "host allocation failed");
+    }
+    UW_HIP(hipMemcpy(words.data(), h->d_words, hd.words * 4, hipMemcpyDeviceToHost));
+    UW_HIP(hipMemcpy(offsets.data(), h->d_offsets, hd.offsets * 4, hipMemcpyDeviceToHost));
+    UW_HIP(hipMemcpy(sm.data(), h->d_sm, n, hipMemcpyDeviceToHost));
+    pw = words.data();
+    po = offsets.data();
+    ps = sm.data();
+  }
+  FileCloser fc{fopen(path, "wb")};
+  if (!fc.f) return fail(UW_ERR_IO, "cannot create %s", path);
+  auto write = [&](const void* src, size_t bytes) { return bytes == 0 || fwrite(src, 1, bytes, fc.f) == bytes; };
+  if (!write(&hd, sizeof hd) || !write(f.hist, sizeof f.hist) || !write(po, hd.offsets * 4) ||
+      !write(pw, hd.words * 4) || !write(ps, n))
+    return fail(UW_ERR_IO, "write to %s failed", path);
+  const int rc = fclose(fc.f);
+  fc.f = nullptr;
+  if (rc != 0) return fail(UW_ERR_IO, "closing %s failed", path);
+  return UW_OK;
+}
+
+uw_status uw_load(const char* path, uint32_t formats, uw_handle* out) {
+  if (!out) return fail(UW_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  if (!path) return fail(UW_ERR_INVALID_ARG, "null path");
+  const uint32_t fmt = formats & 0x7u;
+  if (!fmt) return fail(UW_ERR_INVALID_ARG, "no format requested");
+  if (formats & ~(0x7u | UW_ENC_HOST_ONLY)) return fail(UW_ERR_INVALID_ARG, "unknown format flags 0x%x", formats);
+  const bool host_only = (formats & UW_ENC_HOST_ONLY) != 0;
+  if (host_only && fmt != UW_FMT_HUFFMAN)
+    return fail(UW_ERR_UNSUPPORTED, "palette tables of a bundle are built on the device (no UW_ENC_HOST_ONLY)");
+  uw_matrix* h = new (std::nothrow) uw_matrix;
+  if (!h) return fail(UW_ERR_OOM, "host allocation failed");
+  h->host_only = host_only;
+  uw_status st = load_impl(path, fmt, h);
+  if (st != UW_OK) {
+    if (h->dmem) (void)hipFree(h->dmem);
+    if (h->prep_done) (void)hipEventDestroy(h->prep_done);
+    delete h;
+    return st;
+  }
+  *out = h;
   return UW_OK;
 }
 

@@ -56,7 +56,9 @@ typedef enum {
   UW_ERR_FORMAT = 5,        /* stream too long for 32-bit offsets, bad table  */
   UW_ERR_UNSUPPORTED = 6,   /* pipeline needs a format the handle lacks, or a
                                device call on a host-only handle              */
-  UW_ERR_NO_DEVICE = 7      /* no gfx950 device visible                       */
+  UW_ERR_NO_DEVICE = 7,     /* no gfx950 device visible                       */
+  UW_ERR_IO = 8             /* a bundle file cannot be opened, read or written,
+                               or is not a bundle                             */
 } uw_status;
 
 /* Section 六: the four pipelines.  UW_P_AUTO picks from the plan set with
@@ -193,6 +195,32 @@ uw_status uw_export(uw_handle h, int which, void* dst, size_t cap, size_t* len);
  * one matrix at distinct addresses, e.g. to rotate weight copies past the
  * 256 MB Infinity Cache when measuring HBM throughput. */
 uw_status uw_clone(uw_handle h, uw_handle* out);
+
+/* Distribution bundle (section 十: the bundle that ships every MLP matrix
+ * compressed): write h's Huffman form to the file `path` (created or
+ * truncated).  Layout, little-endian: a 64-byte header {char[8] "UWBUNDLE";
+ * u32 version = 1; u32 header bytes = 64; i64 rows; i64 cols; u64 stream
+ * bits; u32 chunk = 256; u32 code-length limit = 12; u64 payload words; u64
+ * chunk offsets}, the exponent histogram (256 x u64; the canonical code is
+ * rebuilt from it), the chunk bit offsets (u32 each), the payload words (u32,
+ * bits MSB first) and the serial sign+mantissa bytes.  h must hold
+ * UW_FMT_HUFFMAN (else UW_ERR_UNSUPPORTED); a device handle's streams are
+ * copied back to the host first.  UW_ERR_IO if the file cannot be written. */
+uw_status uw_save(uw_handle h, const char* path);
+
+/* Read a bundle written by uw_save into a new handle holding `formats`
+ * (section 六: the direct-palette pipeline reads weights transcoded to the
+ * 4-bit form at model load).  UW_FMT_HUFFMAN uploads the stream as read;
+ * UW_FMT_PALETTE and UW_FMT_RAWAUX are built on the current device from the
+ * Huffman form: the exponents are decoded, the palette is chosen from the
+ * histogram (the encoder's rule), and kernels write the raw-group tables and
+ * the 4-bit codes -- the same bytes uw_encode builds on the host.  With
+ * UW_ENC_HOST_ONLY only UW_FMT_HUFFMAN is allowed (UW_ERR_UNSUPPORTED
+ * otherwise).  Synchronous: the device work has finished on return.  Errors:
+ * UW_ERR_IO (cannot open, not a bundle, truncated), UW_ERR_FORMAT (version,
+ * table sizes, histogram, stream length or chunk offsets inconsistent, or
+ * bytes after the end), UW_ERR_SHAPE, UW_ERR_OOM, UW_ERR_HIP. */
+uw_status uw_load(const char* path, uint32_t formats, uw_handle* out);
 
 void uw_free(uw_handle h);
 
