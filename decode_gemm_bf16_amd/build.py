@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libuw.so")
 BUILD = os.path.join(HERE, "_build")
 
-SOURCES = ["codec.cpp", "runtime.cpp", "variants.cpp", "fused_small.hip", "fused_mid.hip", "fused_large.hip", "fused_ring.hip", "transcode.hip",
+SOURCES = ["codec.cpp", "runtime.cpp", "variants.cpp", "fused_small.hip", "fused_mid.hip", "fused_large.hip", "fused_ring.hip", "fused_rowk.hip", "transcode.hip",
            "huff_decode.hip", "misc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

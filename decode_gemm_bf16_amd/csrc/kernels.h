@@ -26,11 +26,12 @@ struct FusedW {
 // `ksplit` workgroups (atomic accumulation into a zeroed Y).  Large-batch
 // kernels (tokens > 64): see fused_large.hip.
 struct Variant {
-  int kind;    // 0 = small batch, 1 = large batch, 2 = gemv (x in LDS), 3 = mid (K slices of x in LDS)
-  int waves;   // small/gemv/mid: waves per workgroup
-  int ksplit;  // small: workgroups along K
-  int unroll;  // small: bricks in flight per wave; gemv/mid: ring depth
-  int tile;    // large: tile shape id
+  int kind;    // 0 = small batch, 1 = large batch, 2 = gemv (x in LDS), 3 = mid (K slices of x in LDS),
+               // 4 = rowk (whole K per workgroup, x slices streamed through LDS)
+  int waves;   // small/gemv/mid: waves per workgroup; rowk: waves per brick-row
+  int ksplit;  // small: workgroups along K; rowk: bricks per wave per slice
+  int unroll;  // small: bricks in flight per wave; gemv/mid/rowk: ring depth
+  int tile;    // large: tile shape id; rowk: brick-rows per workgroup
 };
 int variant_count(int64_t tokens);
 bool variant_get(int64_t tokens, int id, Variant* v);  // id 0 = default for (tokens, shape)
@@ -41,6 +42,8 @@ Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_m
 // Activations kept in LDS by the gemv variants: tokens x cols <= kGemvXElems
 // bf16 and at most kGemvKbnMax 64-column bricks per row.
 constexpr int64_t kGemvXElems = 16384;
+// Whether a rowk variant's LDS fits for this shape (else it cannot launch).
+bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v);
 constexpr int64_t kGemvKbnMax = 1024;
 // LDS budget of the mid kernels (a K slice of the activations plus the
 // per-brick tables, or the epilogue's partial sums): two workgroups per CU.

@@ -17,6 +17,8 @@ hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64
                              hipStream_t s);
 hipError_t launch_fused_mid(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                             hipStream_t s);
+hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
+                             hipStream_t s);
 
 namespace {
 
@@ -39,6 +41,13 @@ const Named kSmall[] = {
     // a K slice of x in LDS shared by `waves` brick-rows; {waves, ring depth}
     {{3, 16, 1, 2, 0}, "mid:w16:d2"},     {{3, 8, 1, 2, 0}, "mid:w8:d2"},
     {{3, 16, 1, 3, 0}, "mid:w16:d3"},     {{3, 4, 1, 2, 0}, "mid:w4:d2"},
+    // whole K per workgroup (no split): R brick-rows x P waves each, slices of
+    // P*U bricks of x double-buffered in LDS; {P, U, ring depth D, R}
+    {{4, 4, 2, 2, 4}, "rowk:r4p4u2d2"},   {{4, 4, 2, 4, 4}, "rowk:r4p4u2d4"},
+    {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},   {{4, 2, 2, 2, 4}, "rowk:r4p2u2d2"},
+    {{4, 2, 4, 4, 4}, "rowk:r4p2u4d4"},   {{4, 4, 2, 2, 2}, "rowk:r2p4u2d2"},
+    {{4, 4, 1, 2, 2}, "rowk:r2p4u1d2"},   {{4, 8, 1, 2, 1}, "rowk:r1p8u1d2"},
+    {{4, 8, 1, 2, 2}, "rowk:r2p8u1d2"},
 };
 // large batch: kind 1, {tile, ksplit}
 const Named kLarge[] = {
@@ -103,6 +112,8 @@ void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len) {
     snprintf(buf, len, "gemv:w%d:d%d", v.waves, v.unroll);
   else if (v.kind == 3)
     snprintf(buf, len, "mid:w%d:d%d", v.waves, v.unroll);
+  else if (v.kind == 4)
+    snprintf(buf, len, "rowk:r%dp%du%dd%d", v.tile, v.waves, v.ksplit, v.unroll);
   else
     snprintf(buf, len, "small:w%d:k%d:u%d", v.waves, v.ksplit, v.unroll);
 }
@@ -129,6 +140,11 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
     if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128) return Variant{2, 8, 1, 2, 0};
+    // from 12 tokens (20 for matrices too short to fill the chip without a
+    // K split): four brick-rows per workgroup over the whole of K, the
+    // activations streamed through LDS in 8-brick slices
+    const Variant rowk{4, 4, 2, 2, 4};
+    if (tokens >= 12 && (tokens >= 20 || (brows + 3) / 4 >= 128) && rowk_fits(tokens, rows, cols, rowk)) return rowk;
     // from 16 tokens: K slices of the activations in LDS shared by 8
     // brick-rows (the small kernel reads them from L2 once per brick-row)
     if (tokens >= 16) return Variant{3, 8, 1, 2, 0};
@@ -156,12 +172,15 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
 
 Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_mode, const Variant& v0) {
   Variant v = v0;
-  v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, cols / 64));
+  // (kinds 0 and 1 split K across workgroups; rowk's field is its slice shape)
+  if (v.kind == 0 || v.kind == 1) v.ksplit = (int)std::max<int64_t>(1, std::min<int64_t>(v.ksplit, cols / 64));
   // x in LDS where it fits; elsewhere (exponent form, more activations) the
   // same choice falls back to the small kernel's default shape
   if (tokens <= 64 && v.kind == 2 &&
       !(!exp_mode && tokens <= 16 && tokens * cols <= kGemvXElems && cols / 64 <= kGemvKbnMax))
     v = small_default(tokens, rows, cols);
+  // a whole-K shape whose slices and tables do not fit LDS: the K-slice kernel
+  if (tokens <= 64 && v.kind == 4 && !rowk_fits(tokens, rows, cols, v)) v = Variant{3, 8, 1, 2, 0};
   return v;
 }
 
@@ -171,6 +190,7 @@ hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t to
   if (tokens <= 64) {
     if (v.kind == 2) return launch_fused_gemv(w, x, y, tokens, v, s);
     if (v.kind == 3) return launch_fused_mid(w, x, y, tokens, v, s);
+    if (v.kind == 4) return launch_fused_rowk(w, x, y, tokens, v, s);
     if (v.kind != 0) return hipErrorInvalidValue;
     return launch_fused_small(w, x, y, tokens, v, s);
   }

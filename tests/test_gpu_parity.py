@@ -156,7 +156,26 @@ def test_ragged_k_slices_and_ring_tails(env, tokens):
     ref = oracle.matmul_fp64(x, w)
     m = _both(env, w)
     names = uw.variants(tokens)
-    picked = [v for v, n in enumerate(names) if n.startswith(("mid", "large:t1", "small:default", "large:default"))]
+    picked = [v for v, n in enumerate(names)
+              if n.startswith(("mid", "rowk", "large:t1", "small:default", "large:default"))]
+    assert picked
+    for v in picked:
+        for p in (2, 4):
+            y = _run(env, m, x, p, variant=v)
+            assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
+
+
+@pytest.mark.parametrize("tokens", [5, 17, 64])
+def test_rowk_fewer_bricks_than_waves(env, tokens):
+    """2 bricks along K and 3 brick-rows: most waves of a whole-K workgroup
+    own no brick, and the last workgroup has absent brick-rows."""
+    torch, uw = env
+    w = synth.weights(48, 128, 9, 0.02, 10)
+    x = synth.activations(tokens, 128, xseed=5)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    names = uw.variants(tokens)
+    picked = [v for v, n in enumerate(names) if n.startswith("rowk")]
     assert picked
     for v in picked:
         for p in (2, 4):
