@@ -55,7 +55,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int RB2, int TB2, int D, int X, bool EXPM>
+template <int RB2, int TB2, int D, int X, int BPF, bool EXPM>
 __global__ __launch_bounds__(256) void fused_ring_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
@@ -257,21 +257,27 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
     load_w(wcur, kb + D, true);
     issue_x(kb + X - 1);
     const uint8_t* xb = ring_lds + (kb % X) * TILE;
-    u32x4 bf[2];
-    bf[0] = *(const u32x4*)(xb + bsw[0]);
+    // B fragments are read BPF groups ahead (one wave per SIMD: nothing else
+    // hides the LDS latency), from a ring of BPF + 1 registers
+    constexpr int NG = 4 * TB2, NB = BPF + 1;
+    auto read_b = [&](int g) {
+      const int ph = g / TB2, t = g % TB2;
+      return *(const u32x4*)(xb + t * 4096 + bsw[ph]);
+    };
+    u32x4 bf[NB];
 #pragma unroll
-    for (int jj = 0; jj < 4 * TB2; ++jj) {
+    for (int g = 0; g < BPF && g < NG; ++g) bf[g] = read_b(g);
+#pragma unroll
+    for (int jj = 0; jj < NG; ++jj) {
       const int ph = jj / TB2, t = jj % TB2;
-      if (jj + 1 < 4 * TB2) {
-        const int ph1 = (jj + 1) / TB2, t1 = (jj + 1) % TB2;
-        bf[(jj + 1) & 1] = *(const u32x4*)(xb + t1 * 4096 + bsw[ph1]);
-      }
-      const bf16x8 bv = as_bf16x8(bf[jj & 1]);
+      if (jj + BPF < NG) bf[(jj + BPF) % NB] = read_b(jj + BPF);
+      const bf16x8 bv = as_bf16x8(bf[jj % NB]);
 #pragma unroll
       for (int i = 0; i < RB2; ++i)
         acc[i][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[i][ph >> 1][ph & 1], bv, acc[i][t], 0, 0, 0);
     }
     rebuild(wnext, an);
+    if constexpr (BPF > 1) __builtin_amdgcn_sched_group_barrier(0x100, BPF, 0);  // the first B reads
 #pragma unroll
     for (int jj = 0; jj < 4 * TB2 * RB2; ++jj) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
   }
 }
 
-template <int RB2, int TB2, int D, int X>
+template <int RB2, int TB2, int D, int X, int BPF = 1>
 hipError_t launch_ring_t(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, hipStream_t s) {
   const int n_tblk = (int)((tokens + 32 * TB2 - 1) / (32 * TB2));
   const int brows = (int)(w.rows / 16);
@@ -324,7 +330,7 @@ hipError_t launch_ring_t(const FusedW& w, const uint16_t* x, float* y, int64_t t
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   const dim3 grid((unsigned)(n_tblk * n_rblk));
 #define UW_LAUNCH(E)                                                                                              \
-  hipLaunchKernelGGL((fused_ring_kernel<RB2, TB2, D, X, E>), grid, dim3(256), lds, s, w.sm, w.codes, w.meta,     \
+  hipLaunchKernelGGL((fused_ring_kernel<RB2, TB2, D, X, BPF, E>), grid, dim3(256), lds, s, w.sm, w.codes, w.meta,     \
                      w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y, (int)tokens,             \
                      (int)w.rows, (int)w.cols, n_tblk, n_rblk, w.codes_bytes, (int)w.codes_ilv)
   if (w.exp_mode)
@@ -339,7 +345,8 @@ hipError_t launch_ring_t(const FusedW& w, const uint16_t* x, float* y, int64_t t
 
 // tile ids 12..: 12 = 4 waves x (32 rows x 128 tokens), D 4, X 3; 13 = 4 waves x
 // (32 rows x 64 tokens), D 4, X 3; 14 = 4 waves x (64 rows x 128 tokens), D 2, X 3;
-// 15 = 12 with X 8; 16 = 13 with X 8; 17 = 12 with D 6, X 6
+// 15 = 12 with X 8; 16 = 13 with X 8; 17 = 12 with D 6, X 6; 18-21: 12, 16, 15 and 14
+// with the B fragments read 3, 3, 4 and 2 groups ahead (the others read one ahead)
 hipError_t launch_fused_ring(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int tile, hipStream_t s) {
   switch (tile) {
     case 12: return launch_ring_t<1, 4, 4, 3>(w, x, y, tokens, s);
@@ -348,6 +355,10 @@ hipError_t launch_fused_ring(const FusedW& w, const uint16_t* x, float* y, int64
     case 15: return launch_ring_t<1, 4, 4, 8>(w, x, y, tokens, s);
     case 16: return launch_ring_t<1, 2, 4, 8>(w, x, y, tokens, s);
     case 17: return launch_ring_t<1, 4, 6, 6>(w, x, y, tokens, s);
+    case 18: return launch_ring_t<1, 4, 4, 3, 3>(w, x, y, tokens, s);
+    case 19: return launch_ring_t<1, 2, 4, 8, 3>(w, x, y, tokens, s);
+    case 20: return launch_ring_t<1, 4, 4, 8, 4>(w, x, y, tokens, s);
+    case 21: return launch_ring_t<2, 4, 2, 3, 2>(w, x, y, tokens, s);
     default: return hipErrorInvalidValue;
   }
 }

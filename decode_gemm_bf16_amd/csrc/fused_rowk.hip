@@ -134,7 +134,7 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
   };
   // activations of slice j: 16-byte pieces, S*8 per token
   constexpr int PER_TOK = S * 8;
-  constexpr int NXV = (64 * PER_TOK + NT - 1) / NT;
+  constexpr int NXV = (TB * 16 * PER_TOK + NT - 1) / NT;
   const int pieces = tokens * PER_TOK;
   u32x4 xv[NXV];
   auto issue_x = [&](int j) {
@@ -236,6 +236,7 @@ hipError_t launch_rowk_t(const FusedW& w, const uint16_t* x, float* y, int64_t t
 template <int R, int P, int U, int D>
 hipError_t launch_rowk_c(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int kper, int ksplit,
                          size_t lds, hipStream_t s) {
+  if (tokens > 64) return hipErrorInvalidValue;
   switch ((tokens + 15) / 16) {
     case 1: return launch_rowk_t<R, P, U, D, 1>(w, x, y, tokens, kper, ksplit, lds, s);
     case 2: return launch_rowk_t<R, P, U, D, 2>(w, x, y, tokens, kper, ksplit, lds, s);
@@ -246,10 +247,13 @@ hipError_t launch_rowk_c(const FusedW& w, const uint16_t* x, float* y, int64_t t
 
 }  // namespace
 
+// token blocks of 16 the kernel is instantiated with for `tokens`
+int rowk_tb(int64_t tokens) { return tokens <= 64 ? (int)((tokens + 15) / 16) : tokens <= 96 ? 6 : 8; }
+
 size_t rowk_lds_bytes(int64_t tokens, int kper, int r, int p, int u) {
   const size_t xrow = (size_t)p * u * 128 + 16;
   const size_t in = 2 * (size_t)tokens * xrow + 32 + (size_t)r * kper * 8;
-  const size_t red = (size_t)r * p * ((tokens + 15) / 16) * 64 * 16;
+  const size_t red = (size_t)r * p * rowk_tb(tokens) * 64 * 16;
   return std::max(in, red);
 }
 
@@ -270,12 +274,15 @@ size_t rowk_plan(int64_t tokens, int64_t rows, int64_t cols, const Variant& v, i
 }
 
 bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v) {
-  return tokens >= 1 && tokens <= 64 && rowk_plan(tokens, rows, cols, v, nullptr, nullptr) <= kRowkLdsBytes;
+  if (tokens < 1 || tokens > 128) return false;
+  // above 64 tokens only the R4 P4 U1 shape is built
+  if (tokens > 64 && !(v.tile == 4 && v.waves == 4 && v.ksplit == 1 && v.unroll == 2)) return false;
+  return rowk_plan(tokens, rows, cols, v, nullptr, nullptr) <= kRowkLdsBytes;
 }
 
 hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                              hipStream_t s) {
-  if (tokens < 1 || tokens > 64) return hipErrorInvalidValue;
+  if (!rowk_fits(tokens, w.rows, w.cols, v)) return hipErrorInvalidValue;
   const int R = v.tile, P = v.waves, U = v.ksplit, D = v.unroll;
   int kper = 0, ks = 0;
   const size_t lds = rowk_plan(tokens, w.rows, w.cols, v, &kper, &ks);
@@ -283,6 +290,10 @@ hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64
   if (ks > 1) {
     hipError_t e = launch_zero(y, tokens * w.rows, s);
     if (e != hipSuccess) return e;
+  }
+  if (tokens > 64) {  // 65..128 tokens: 6 or 8 token blocks
+    if (tokens <= 96) return launch_rowk_t<4, 4, 1, 2, 6>(w, x, y, tokens, kper, ks, lds, s);
+    return launch_rowk_t<4, 4, 1, 2, 8>(w, x, y, tokens, kper, ks, lds, s);
   }
 #define UW_CASE(RR, PP, UU, DD) \
   if (R == RR && P == PP && U == UU && D == DD)  \

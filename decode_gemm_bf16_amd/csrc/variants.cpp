@@ -75,6 +75,12 @@ const Named kLarge[] = {
     {{1, 0, 1, 0, 15}, "large:t15(4x32r x128t,32x32,ring d4 x8)"},
     {{1, 0, 1, 0, 16}, "large:t16(4x32r x64t,32x32,ring d4 x8)"},
     {{1, 0, 1, 0, 17}, "large:t17(4x32r x128t,32x32,ring d6 x6)"},
+    {{1, 0, 1, 0, 18}, "large:t18(4x32r x128t,32x32,ring d4 x3 b3)"},
+    {{1, 0, 1, 0, 19}, "large:t19(4x32r x64t,32x32,ring d4 x8 b3)"},
+    {{1, 0, 1, 0, 20}, "large:t20(4x32r x128t,32x32,ring d4 x8 b4)"},
+    {{1, 0, 1, 0, 21}, "large:t21(4x64r x128t,32x32,ring d2 x3 b2)"},
+    // whole K per workgroup, 16x16x32 instructions, up to 128 tokens
+    {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -150,6 +156,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     if (tokens >= 16) return Variant{3, 8, 1, 2, 0};
     return small_default(tokens, rows, cols);
   }
+  // up to 128 tokens: the whole-K kernel (16x16x32 instructions, four waves
+  // per SIMD, activations streamed through LDS in 4-brick slices)
+  const Variant rowk{4, 4, 1, 2, 4};
+  if (tokens <= 128 && rowk_fits(tokens, rows, cols, rowk)) return rowk;
   // 256 x 256 tiles with the rebuild interleaved into the MFMAs once there are
   // enough tokens to fill the chip with them (one workgroup per CU)
   const int64_t wg11 = ((brows + 15) / 16) * ((tokens + 255) / 256);
@@ -179,8 +189,10 @@ Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_m
   if (tokens <= 64 && v.kind == 2 &&
       !(!exp_mode && tokens <= 16 && tokens * cols <= kGemvXElems && cols / 64 <= kGemvKbnMax))
     v = small_default(tokens, rows, cols);
-  // a whole-K shape whose slices and tables do not fit LDS: the K-slice kernel
-  if (tokens <= 64 && v.kind == 4 && !rowk_fits(tokens, rows, cols, v)) v = Variant{3, 8, 1, 2, 0};
+  // a whole-K shape whose slices and tables do not fit LDS (or more tokens
+  // than it is built for): the K-slice kernel, or the large-batch default
+  if (v.kind == 4 && !rowk_fits(tokens, rows, cols, v))
+    v = tokens <= 64 ? Variant{3, 8, 1, 2, 0} : variant_default(tokens, rows, cols);
   return v;
 }
 
@@ -194,6 +206,7 @@ hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t to
     if (v.kind != 0) return hipErrorInvalidValue;
     return launch_fused_small(w, x, y, tokens, v, s);
   }
+  if (v.kind == 4) return launch_fused_rowk(w, x, y, tokens, v, s);
   if (v.kind != 1) return hipErrorInvalidValue;
   return launch_fused_large(w, x, y, tokens, v, s);
 }

@@ -143,7 +143,7 @@ def test_every_variant(env, tokens):
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p)
 
 
-@pytest.mark.parametrize("tokens", [17, 40, 64, 100, 200])
+@pytest.mark.parametrize("tokens", [17, 40, 64, 80, 100, 128, 200])
 def test_ragged_k_slices_and_ring_tails(env, tokens):
     """K of 27 bricks (1728 columns), 34 brick-rows: the mid kernels split K
     into slices of unequal length (float atomics into a zeroed Y), the ring
