@@ -26,7 +26,7 @@ import math
 import sys
 import time
 
-from . import (FMT_HUFFMAN, FMT_PALETTE, Matrix, mlp_forward, mlp_workspace_bytes, variant_name, variants,
+from . import (FMT_HUFFMAN, FMT_PALETTE, Matrix, mlp_forward, mlp_workspace_bytes, variants,
                stack_forward, stack_workspace_bytes, stream_create, stream_destroy, device_cu_count, bf16_tensor)
 
 PROJECTIONS = ("gate", "up", "down")
@@ -107,11 +107,27 @@ def time_projection(torch, mats, x, y, tokens: int, pipeline: int, variant: int,
     return time_graph(torch, fn, steps, 3, stream)
 
 
+def effective_name(mat: Matrix, tokens: int, pipeline: int, variant: int) -> str:
+    """The kernel that (pipeline, variant) launches for this shape (variants
+    that do not apply fall back to their family's default; pipeline 1 is the
+    library GEMM whatever the variant)."""
+    mat.set_variant(variant)
+    name = mat.variant_in_use(tokens, pipeline)[1]
+    mat.set_variant(0)
+    return name
+
+
 def rank_projection(torch, mats, x, y, tokens: int, stream, keep: int = 4, steps: int = 20) -> list[tuple]:
-    """All (pipeline, variant) pairs of one projection, fastest first."""
+    """All distinct (pipeline, kernel) choices of one projection, fastest
+    first, as (ms, pipeline, variant id)."""
     res = []
+    seen = set()
     for p in candidates(mats[0]):
         for v in range(len(variants(tokens))):
+            key = (p, effective_name(mats[0], tokens, p, v))
+            if key in seen:  # the same kernel under another id
+                continue
+            seen.add(key)
             ms = time_projection(torch, mats, x, y, tokens, p, v, stream, steps)
             res.append((ms, p, v))
     res.sort()
@@ -179,7 +195,7 @@ def tune_mlp(torch, layer: dict, tokens_list, stream, steps: int = 10, keep: int
                 m.set_variant(0)
         entry = {proj: list(choice[proj]) for proj in PROJECTIONS}
         entry["layer_us"] = round(best * 1e3, 2)
-        entry["variant_names"] = {proj: variant_name(tokens, choice[proj][1]) for proj in PROJECTIONS}
+        entry["variant_names"] = {proj: effective_name(layer[proj][0], tokens, *choice[proj]) for proj in PROJECTIONS}
         entry["rounds"] = rounds
         plan["batches"][str(tokens)] = entry
         log(f"tokens {tokens}: {json.dumps(entry)} ({time.perf_counter() - t0:.1f} s)")
