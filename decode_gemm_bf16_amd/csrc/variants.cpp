@@ -164,9 +164,15 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   // enough tokens to fill the chip with them (one workgroup per CU)
   const int64_t wg11 = ((brows + 15) / 16) * ((tokens + 255) / 256);
   if (tokens >= 512 && wg11 >= 192) return Variant{1, 0, 1, 0, 11};
-  // below that, the deep-prefetch tiles (128 rows) where they fill the chip
+  // below that, the deep-prefetch tiles (128 rows; 128 tokens, B fragments
+  // read three groups ahead, where that fills the chip, else 64 tokens).
+  // They do not split K: for K of 256 bricks and more the K-split tiles
+  // below do better.
   const int64_t rb8 = (brows + 7) / 8;
-  if (rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, tokens <= 192 ? 13 : 16};
+  if (kbn < 256) {
+    if (rb8 * ((tokens + 127) / 128) >= 192) return Variant{1, 0, 1, 0, 18};
+    if (rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, tokens <= 192 ? 13 : 16};
+  }
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
   const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tiles 1/5: 128 rows per workgroup
