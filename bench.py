@@ -262,6 +262,71 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
     return out
 
 
+# Other projection shapes, synthetic weights of the same recipe: SwiGLU MLPs
+# of other sizes and the attention projections and vocabulary projection of
+# the 8B-shaped model (rows x cols of W).
+OTHER_SHAPES = [
+    ("mlp 18944x3584 gate/up (Qwen2.5-7B-sized)", 18944, 3584),
+    ("mlp 3584x18944 down (Qwen2.5-7B-sized)", 3584, 18944),
+    ("mlp 14336x5120 gate/up (Mistral-NeMo-12B-sized)", 14336, 5120),
+    ("mlp 5120x14336 down (Mistral-NeMo-12B-sized)", 5120, 14336),
+    ("mlp 8192x3072 gate/up (Llama-3.2-3B-sized)", 8192, 3072),
+    ("mlp 3072x8192 down (Llama-3.2-3B-sized)", 3072, 8192),
+    ("attention 4096x4096 q/o (8B-sized)", 4096, 4096),
+    ("attention 1024x4096 k/v (8B-sized, 8 KV heads)", 1024, 4096),
+    ("vocabulary 128256x4096 output projection (8B-sized)", 128256, 4096),
+]
+
+
+def shapes_bench(torch, uw, synth, stream, steps, warmup, tokens_list=(1, 16, 64)) -> dict:
+    """Direct palette (P4, built-in kernel choice) against the uncompressed
+    hipBLASLt GEMM on other projection shapes; copies of each matrix rotated
+    past the Infinity Cache as in the main measurement."""
+    c = synth.CONFIGS["mlp_8b"]
+    out = {}
+    for i, (name, rows, cols) in enumerate(OTHER_SHAPES):
+        w = synth.weights(rows, cols, 100 + i, c["p"], c["shift"])
+        base = uw.Matrix(w, uw.FMT_PALETTE | uw.FMT_HUFFMAN)
+        info = base.info()
+        ncopy = max(2, math.ceil((1 << 30) / info["resident_bytes"]))
+        mats = [base] + [base.clone() for _ in range(ncopy - 1)]
+        for m in mats:
+            m.set_streams(stream)
+        nwd = max(2, math.ceil((1 << 30) / (2 * rows * cols)))
+        wds = [uw.bf16_tensor(w) for _ in range(nwd)]
+        del w
+        res = {"rows": rows, "cols": cols, "bpw_palette": round(info["bpw_palette"], 4),
+               "bpw_huffman": round(info["bpw_huffman"], 4)}
+        xs = synth.activations(max(tokens_list), cols, xseed=1)
+        for tokens in tokens_list:
+            x = uw.bf16_tensor(xs[:tokens])
+            y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
+            k = [0]
+
+            def fn(x=x, y=y, tokens=tokens):
+                mats[k[0] % ncopy].matmul(x, y, tokens, uw.P4_DIRECT_PALETTE)
+                k[0] += 1
+            ms = time_graph(torch, fn, steps=max(20, steps // 10), warmup=warmup, stream=stream)
+            j = [0]
+
+            def blas(x=x, y=y, tokens=tokens):
+                uw.gemm_bf16(x, wds[j[0] % nwd], y, tokens, rows, cols, stream)
+                j[0] += 1
+            bms = time_graph(torch, blas, steps=max(20, steps // 10), warmup=warmup, stream=stream)
+            res[str(tokens)] = {"P4_us": round(ms * 1e3, 2), "bf16_hipblaslt_us": round(bms * 1e3, 2),
+                                "P4_eff_GBps": round(2.0 * rows * cols / ms / 1e6, 1),
+                                "P4_algo_GBps": round(rows * cols * info["bpw_palette"] / 8 / ms / 1e6, 1),
+                                "speedup": round(bms / ms, 3),
+                                "kernel": base.variant_in_use(tokens, uw.P4_DIRECT_PALETTE)[1]}
+        log(f"{name}: " + json.dumps(res))
+        out[name] = res
+        for m in mats:
+            m.free()
+        del wds, mats, base
+        torch.cuda.empty_cache()
+    return out
+
+
 def bundle_load_bench(uw, w, reps: int = 3) -> dict:
     """The gate's Huffman form written to a bundle file, then loaded straight
     into the direct-palette form (the exponents decoded and transcoded to 4-bit
@@ -304,6 +369,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
+    ap.add_argument("--shapes", action="store_true",
+                    help="also time the direct palette on other MLP, attention and vocabulary shapes")
     ap.add_argument("--load", action="store_true",
                     help="also time a bundle file of the gate loaded into the palette form (device transcode)")
     args = ap.parse_args()
@@ -443,6 +510,8 @@ def main() -> int:
         torch.cuda.empty_cache()
     if args.load:
         result["bundle_load"] = bundle_load_bench(uw, w)
+    if args.shapes:
+        result["shapes"] = shapes_bench(torch, uw, synth, stream, args.steps, args.warmup)
     if args.stack:
         for m in mats:
             m.free()

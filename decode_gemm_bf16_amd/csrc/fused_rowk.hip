@@ -260,12 +260,13 @@ size_t rowk_lds_bytes(int64_t tokens, int kper, int r, int p, int u) {
 size_t rowk_plan(int64_t tokens, int64_t rows, int64_t cols, const Variant& v, int* kper_out, int* ks_out) {
   const int R = v.tile, P = v.waves, U = v.ksplit, S = P * U;
   // Split K only when the workgroups (one per R brick-rows) would leave most
-  // CUs idle: into ranges of whole slices, at most one per 256 CUs' worth
-  // and at least two slices long; the ranges then add into a zeroed Y.
+  // CUs idle: into ranges of whole slices, at least two slices long, and no
+  // more workgroups than CUs (one per CU when the slices are large); the
+  // ranges then add into a zeroed Y.
   const int kbn = (int)(cols / 64);
   const int64_t groups = (rows / 16 + R - 1) / R;
   int ks = 1;
-  if (groups < 128) ks = (int)std::max<int64_t>(1, std::min<int64_t>((256 + groups - 1) / groups, kbn / (2 * S)));
+  if (groups < 128) ks = (int)std::max<int64_t>(1, std::min<int64_t>(256 / groups, kbn / (2 * S)));
   const int kper = ((kbn + ks - 1) / ks + S - 1) / S * S;
   ks = (kbn + kper - 1) / kper;
   if (kper_out) *kper_out = kper;

@@ -149,8 +149,12 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // from 12 tokens (20 for matrices too short to fill the chip without a
     // K split): four brick-rows per workgroup over the whole of K, the
     // activations streamed through LDS in 8-brick slices
-    const Variant rowk{4, 4, 2, 2, 4};
-    if (tokens >= 12 && (tokens >= 20 || (brows + 3) / 4 >= 128) && rowk_fits(tokens, rows, cols, rowk)) return rowk;
+    // (two waves per brick-row and 4-brick slices when 4-brick-row
+    // workgroups would need a second round on the CUs: half the LDS, two
+    // workgroups per CU)
+    const int64_t groups = (brows + 3) / 4;
+    const Variant rowk = groups > 256 && groups <= 512 ? Variant{4, 2, 2, 2, 4} : Variant{4, 4, 2, 2, 4};
+    if (tokens >= 12 && (tokens >= 20 || groups >= 128) && rowk_fits(tokens, rows, cols, rowk)) return rowk;
     // from 16 tokens: K slices of the activations in LDS shared by 8
     // brick-rows (the small kernel reads them from L2 once per brick-row)
     if (tokens >= 16) return Variant{3, 8, 1, 2, 0};

@@ -183,6 +183,24 @@ def test_rowk_fewer_bricks_than_waves(env, tokens):
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
 
 
+@pytest.mark.parametrize("rows,cols", [(1024, 4096), (3584, 18944), (128256, 4096)])
+def test_other_projection_shapes(env, rows, cols):
+    """Attention k/v (1024 x 4096), a wider MLP's down projection
+    (3584 x 18944) and the vocabulary projection (128256 x 4096): direct
+    palette with the built-in kernel choice, sampled rows against fp64."""
+    torch, uw = env
+    w = synth.weights(rows, cols, 21, 0.0005, 10)
+    m = uw.Matrix(w, uw.FMT_PALETTE)
+    sample = np.random.default_rng(1).choice(rows, min(rows, 384), replace=False)
+    for tokens in ((1, 16, 64, 100) if rows * cols < (1 << 28) else (1, 16)):
+        print(f"shape {rows}x{cols} tokens {tokens}", flush=True)
+        x = synth.activations(tokens, cols, xseed=tokens)
+        y = _run(env, m, x, uw.P4_DIRECT_PALETTE)
+        assert not np.isnan(y).any()
+        ref = oracle.matmul_fp64_rows(x, w, sample)
+        assert oracle.rel_err(y[:, sample], ref) <= TOL, (rows, cols, tokens)
+
+
 def test_gate_full_size_batch1(env):
     """14336x4096 gate, batch 1 (the headline workload): full decode bit-exact,
     resident codes bit-exact, sampled outputs of all pipelines vs fp64."""
