@@ -327,6 +327,100 @@ def shapes_bench(torch, uw, synth, stream, steps, warmup, tokens_list=(1, 16, 64
     return out
 
 
+def moe_bench(torch, uw, synth, stream, steps, warmup, n_experts=8, top_k=2, tokens_list=(1, 16, 64)) -> dict:
+    """Cold experts: eight 14336 x 4096 expert projections (Mixtral-8x7B-sized
+    w1) kept compressed in page-locked host memory and uploaded on demand --
+    the bytes and time of one upload against the bf16 matrix, also from
+    page-locked memory -- then top-2 routed tokens
+    through the grouped fused matmul against per-expert hipBLASLt GEMMs on
+    bf16 copies.  Routings alternate so that consecutive calls touch
+    different experts (no Infinity-Cache reuse)."""
+    import numpy as np
+    c = synth.CONFIGS["mlp_8b"]
+    rows, cols = 14336, 4096
+    ws = [synth.weights(rows, cols, 200 + e, c["p"], c["shift"]) for e in range(n_experts)]
+    res = {"experts": n_experts, "top_k": top_k, "rows": rows, "cols": cols}
+    # on-demand uploads from pageable host memory, one expert at a time
+    up = {}
+    for label, fmt in (("palette", uw.FMT_PALETTE), ("huffman", uw.FMT_HUFFMAN)):
+        ms_, nbytes = [], 0
+        for w in ws[:4]:
+            m = uw.Matrix(w, fmt | uw.ENC_HOST_ONLY)
+            m.upload()  # the first upload also builds the page-locked image
+            m.evict()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            m.upload()
+            torch.cuda.synchronize()
+            ms_.append((time.perf_counter() - t0) * 1e3)
+            nbytes = m.info()["resident_bytes"]
+            m.free()
+        up[label] = {"ms": round(sorted(ms_)[len(ms_) // 2], 3), "bytes": nbytes}
+    ms_ = []
+    for w in ws[:4]:
+        hw = torch.from_numpy(w.view(np.int16)).pin_memory()
+        dw = torch.empty_like(hw, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dw.copy_(hw)
+        torch.cuda.synchronize()
+        ms_.append((time.perf_counter() - t0) * 1e3)
+        del dw
+    up["bf16"] = {"ms": round(sorted(ms_)[len(ms_) // 2], 3), "bytes": 2 * rows * cols}
+    res["upload"] = up
+    log("moe upload: " + json.dumps(up))
+    # grouped fused matmul over resident experts (direct palette)
+    experts = [uw.Matrix(w, uw.FMT_PALETTE | uw.ENC_HOST_ONLY) for w in ws]
+    for m in experts:
+        m.upload()
+        m.set_streams(stream)
+    wds = [uw.bf16_tensor(w) for w in ws]
+    rng = np.random.default_rng(5)
+    grouped = {}
+    for tokens in tokens_list:
+        xs = synth.activations(tokens, cols, xseed=tokens)
+        routings = []
+        for r in range(4):
+            if tokens == 1:  # one token: alternate disjoint expert pairs
+                choice = np.array([[2 * r, 2 * r + 1]])
+            else:
+                choice = np.stack([rng.choice(n_experts, top_k, replace=False) for _ in range(tokens)])
+            order = np.argsort(choice.reshape(-1), kind="stable")
+            tok_of = (np.arange(tokens * top_k) // top_k)[order]
+            counts = np.bincount(choice.reshape(-1), minlength=n_experts)
+            offs = np.concatenate([[0], np.cumsum(counts)])
+            x = uw.bf16_tensor(xs[tok_of])
+            routings.append((x, offs.tolist()))
+        nr = tokens * top_k
+        y = torch.empty((nr, rows), device="cuda", dtype=torch.float32)
+        k = [0]
+
+        def fused():
+            x, offs = routings[k[0] % len(routings)]
+            uw.grouped_matmul(experts, x, y, offs, uw.P4_DIRECT_PALETTE)
+            k[0] += 1
+        ms = time_graph(torch, fused, steps=max(20, steps // 10), warmup=warmup, stream=stream)
+        j = [0]
+
+        def blas():
+            x, offs = routings[j[0] % len(routings)]
+            for e in range(n_experts):
+                t = offs[e + 1] - offs[e]
+                if t:
+                    uw.gemm_bf16(x[offs[e]:offs[e + 1]], wds[e], y[offs[e]:offs[e + 1]], t, rows, cols, stream)
+            j[0] += 1
+        bms = time_graph(torch, blas, steps=max(20, steps // 10), warmup=warmup, stream=stream)
+        grouped[str(tokens)] = {"routed_rows": nr, "P4_us": round(ms * 1e3, 2), "bf16_hipblaslt_us": round(bms * 1e3, 2),
+                                "speedup": round(bms / ms, 3)}
+        log(f"moe grouped {tokens}: " + json.dumps(grouped[str(tokens)]))
+    res["grouped"] = grouped
+    for m in experts:
+        m.free()
+    del wds
+    torch.cuda.empty_cache()
+    return res
+
+
 def bundle_load_bench(uw, w, reps: int = 3) -> dict:
     """The gate's Huffman form written to a bundle file, then loaded straight
     into the direct-palette form (the exponents decoded and transcoded to 4-bit
@@ -369,6 +463,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
+    ap.add_argument("--moe", action="store_true",
+                    help="also time cold-expert uploads and the grouped matmul over 8 experts")
     ap.add_argument("--shapes", action="store_true",
                     help="also time the direct palette on other MLP, attention and vocabulary shapes")
     ap.add_argument("--load", action="store_true",
@@ -512,6 +608,8 @@ def main() -> int:
         result["bundle_load"] = bundle_load_bench(uw, w)
     if args.shapes:
         result["shapes"] = shapes_bench(torch, uw, synth, stream, args.steps, args.warmup)
+    if args.moe:
+        result["moe"] = moe_bench(torch, uw, synth, stream, args.steps, args.warmup)
     if args.stack:
         for m in mats:
             m.free()

@@ -26,7 +26,7 @@ FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 
 EXPORTED = [
     "uw_encode", "uw_decode", "uw_matmul", "uw_preprocess", "uw_set_streams", "uw_set_scratch", "uw_set_plan",
-    "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_save", "uw_load", "uw_free", "uw_last_error", "uw_silu_mul",
+    "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_save", "uw_load", "uw_upload", "uw_evict", "uw_grouped_matmul", "uw_free", "uw_last_error", "uw_silu_mul",
     "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_stack_forward", "uw_stack_workspace_bytes",
     "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy", "uw_device_read",
 ]
@@ -86,6 +86,9 @@ def _load() -> C.CDLL:
         "uw_clone": ([vp, C.POINTER(vp)], st),
         "uw_save": ([vp, C.c_char_p], st),
         "uw_load": ([C.c_char_p, u32, C.POINTER(vp)], st),
+        "uw_upload": ([vp], st),
+        "uw_evict": ([vp], st),
+        "uw_grouped_matmul": ([C.POINTER(vp), i32, vp, C.POINTER(i64), vp, C.c_int], st),
         "uw_free": ([vp], None),
         "uw_last_error": ([], C.c_char_p),
         "uw_silu_mul": ([vp, vp, vp, i64, vp], st),
@@ -201,6 +204,14 @@ class Matrix:
         info = m.info()
         m.rows, m.cols = info["rows"], info["cols"]
         return m
+
+    def upload(self) -> None:
+        """Copy a host-only matrix's compressed streams to the device (``uw_upload``)."""
+        _check(_lib.uw_upload(self._h))
+
+    def evict(self) -> None:
+        """Release the device copy of an uploaded matrix (``uw_evict``)."""
+        _check(_lib.uw_evict(self._h))
 
     def decode(self, out) -> None:
         """bf16 W -> ``out`` (device tensor of rows*cols 16-bit elements)."""
@@ -323,3 +334,11 @@ def bits_of(t) -> np.ndarray:
     """bf16/int16 torch tensor -> numpy uint16 bit patterns (host copy)."""
     import torch
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def grouped_matmul(experts, x, y, row_offsets, pipeline: int = P_AUTO) -> None:
+    """y[o[e]:o[e+1]] = x[o[e]:o[e+1]] @ W_e^T for each expert e (``uw_grouped_matmul``)."""
+    n = len(experts)
+    hs = (C.c_void_p * n)(*[m.handle for m in experts])
+    offs = (C.c_int64 * (n + 1))(*[int(v) for v in row_offsets])
+    _check(_lib.uw_grouped_matmul(hs, n, _ptr(x), offs, _ptr(y), pipeline))

@@ -131,6 +131,9 @@ uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, i
 struct uw_matrix {
   uw::HostFormat hf;
   bool host_only = false;
+  bool keep_host = false;  // the host streams stay after uw_upload (for uw_evict / re-upload)
+  void* pinned = nullptr;  // uw_upload: page-locked image of the device allocation
+  size_t pinned_bytes = 0;
   int64_t rows = 0, cols = 0;
   uint32_t formats = 0;
   // one device allocation holding every resident stream
@@ -326,72 +329,118 @@ T* carve(uint8_t*& cur, size_t bytes) {
   return p;
 }
 
-// Allocate the handle's device memory and copy the host streams into it.
-// With device_tables (load-time transcode) the palette tables, codes
-// included, are left for the caller's kernels to write.
-uw_status upload(uw_matrix* h, bool device_tables = false) {
+// Byte offsets of the resident streams in the handle's one device
+// allocation (absent streams: kNone).
+constexpr size_t kNone = ~size_t(0);
+struct Layout {
+  size_t sm = kNone, nib = kNone, meta = kNone, side = kNone, words = kNone, offsets = kNone, lut = kNone,
+         lutc = kNone, total = 0;
+};
+
+Layout layout_of(const uw_matrix* h) {
   const uw::HostFormat& f = h->hf;
-  const uint64_t n = f.n();
-  const uint64_t nb = f.bricks();
-  size_t total = align256(n);  // sm
+  const uint64_t n = f.n(), nb = f.bricks();
   const bool pal = h->has(UW_FMT_PALETTE), tabs = h->has_pal_tables(), huf = h->has(UW_FMT_HUFFMAN);
-  const size_t side_bytes = std::max<size_t>(f.n_raw * 64, 64);
-  if (pal) total += align256(n / 2);
-  if (tabs || huf) total += align256(nb * 8) + align256(side_bytes);
-  if (huf) total += align256(f.words.size() * 4) + align256(f.offsets.size() * 4) + 2 * align256(uw::kLutSize * 4);
-  if (hipMalloc(&h->dmem, total) != hipSuccess) {
-    h->dmem = nullptr;
-    return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", total);
-  }
-  h->dmem_bytes = total;
-  uint8_t* cur = static_cast<uint8_t*>(h->dmem);
-  h->d_sm = carve<uint8_t>(cur, n);
-  UW_HIP(hipMemcpy(h->d_sm, f.sm.data(), n, hipMemcpyHostToDevice));
-  if (pal) {
-    h->d_nib = carve<uint8_t>(cur, n / 2);
-    if (!device_tables) UW_HIP(hipMemcpy(h->d_nib, f.nib.data(), n / 2, hipMemcpyHostToDevice));
-  }
+  Layout L;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur += align256(bytes);
+    return at;
+  };
+  L.sm = take(n);
+  if (pal) L.nib = take(n / 2);
   if (tabs || huf) {
-    h->d_meta = carve<uint2>(cur, nb * 8);
-    if (!device_tables) {
-      // per-brick {raw map, raw groups before}; all zero for a Huffman-only matrix
-      std::vector<uint2> meta(nb, uint2{0, 0});
-      if (tabs)
-        for (uint64_t b = 0; b < nb; ++b) meta[b] = uint2{f.rawmap[b], f.rawbefore[b]};
-      UW_HIP(hipMemcpy(h->d_meta, meta.data(), nb * 8, hipMemcpyHostToDevice));
-    }
-    h->d_side = carve<uint8_t>(cur, side_bytes);
-    if (!device_tables && !f.side.empty())
-      UW_HIP(hipMemcpy(h->d_side, f.side.data(), f.side.size(), hipMemcpyHostToDevice));
+    L.meta = take(nb * 8);
+    L.side = take(std::max<size_t>(f.n_raw * 64, 64));
   }
   if (huf) {
-    h->d_words = carve<uint32_t>(cur, f.words.size() * 4);
-    UW_HIP(hipMemcpy(h->d_words, f.words.data(), f.words.size() * 4, hipMemcpyHostToDevice));
-    h->d_offsets = carve<uint32_t>(cur, f.offsets.size() * 4);
-    UW_HIP(hipMemcpy(h->d_offsets, f.offsets.data(), f.offsets.size() * 4, hipMemcpyHostToDevice));
-    const std::vector<uint32_t> lut3 = uw::multi_symbol_table(f.lut);
-    h->d_lut = carve<uint32_t>(cur, uw::kLutSize * 4);
-    UW_HIP(hipMemcpy(h->d_lut, lut3.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
-    // pipeline 3 decodes straight to palette codes
-    uint8_t code_of[256];
-    std::memset(code_of, 0, sizeof code_of);
-    if (tabs) {
-      const int used = std::min<int>(16, int(f.distinct));
-      for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
-    }
-    const std::vector<uint32_t> lutc = uw::multi_code_table(f.lut, code_of);
-    h->d_lut_codes = carve<uint32_t>(cur, uw::kLutSize * 4);
-    UW_HIP(hipMemcpy(h->d_lut_codes, lutc.data(), uw::kLutSize * 4, hipMemcpyHostToDevice));
-    h->words_total = f.words.size();
+    L.words = take(f.words.size() * 4);
+    L.offsets = take(f.offsets.size() * 4);
+    L.lut = take(uw::kLutSize * 4);
+    L.lutc = take(uw::kLutSize * 4);
   }
-  if (tabs) {
+  L.total = cur;
+  return L;
+}
+
+void assign_pointers(uw_matrix* h, const Layout& L) {
+  uint8_t* base = static_cast<uint8_t*>(h->dmem);
+  auto at = [&](size_t off) { return off == kNone ? nullptr : base + off; };
+  h->d_sm = at(L.sm);
+  h->d_nib = at(L.nib);
+  h->d_meta = reinterpret_cast<uint2*>(at(L.meta));
+  h->d_side = at(L.side);
+  h->d_words = reinterpret_cast<uint32_t*>(at(L.words));
+  h->d_offsets = reinterpret_cast<uint32_t*>(at(L.offsets));
+  h->d_lut = reinterpret_cast<uint32_t*>(at(L.lut));
+  h->d_lut_codes = reinterpret_cast<uint32_t*>(at(L.lutc));
+  h->words_total = h->has(UW_FMT_HUFFMAN) ? h->hf.words.size() : 0;
+  if (h->has_pal_tables()) {
     // palette entry i, exponent rotated right by one bit, at byte i%4 of lut_v[i/4]
+    for (int i = 0; i < 4; ++i) h->lut_v[i] = 0;
     for (int i = 0; i < 16; ++i) {
-      const uint32_t e = f.palette[i];
+      const uint32_t e = h->hf.palette[i];
       const uint32_t v = ((e >> 1) | (e << 7)) & 0xFFu;
       h->lut_v[i / 4] |= v << (8 * (i % 4));
     }
   }
+}
+
+// Hand every host stream to put(offset, bytes, source) at its layout offset,
+// the derived tables (per-brick meta, decode tables) built on the way.  With
+// device_tables the palette codes, meta and side table are skipped (kernels
+// write them).
+template <class Put>
+uw_status put_streams(const uw_matrix* h, const Layout& L, bool device_tables, Put&& put) {
+  const uw::HostFormat& f = h->hf;
+  const uint64_t n = f.n(), nb = f.bricks();
+  uw_status st;
+  if ((st = put(L.sm, n, f.sm.data())) != UW_OK) return st;
+  if (L.nib != kNone && !device_tables && (st = put(L.nib, n / 2, f.nib.data())) != UW_OK) return st;
+  if (L.meta != kNone && !device_tables) {
+    // per-brick {raw map, raw groups before}; all zero for a Huffman-only matrix
+    std::vector<uint2> meta(nb, uint2{0, 0});
+    if (h->has_pal_tables())
+      for (uint64_t b = 0; b < nb; ++b) meta[b] = uint2{f.rawmap[b], f.rawbefore[b]};
+    if ((st = put(L.meta, nb * 8, meta.data())) != UW_OK) return st;
+    if (!f.side.empty() && (st = put(L.side, f.side.size(), f.side.data())) != UW_OK) return st;
+  }
+  if (L.words != kNone) {
+    if ((st = put(L.words, f.words.size() * 4, f.words.data())) != UW_OK) return st;
+    if ((st = put(L.offsets, f.offsets.size() * 4, f.offsets.data())) != UW_OK) return st;
+    const std::vector<uint32_t> lut3 = uw::multi_symbol_table(f.lut);
+    if ((st = put(L.lut, uw::kLutSize * 4, lut3.data())) != UW_OK) return st;
+    // pipeline 3 decodes straight to palette codes
+    uint8_t code_of[256];
+    std::memset(code_of, 0, sizeof code_of);
+    if (h->has_pal_tables()) {
+      const int used = std::min<int>(16, int(f.distinct));
+      for (int i = used - 1; i >= 0; --i) code_of[f.palette[i]] = uint8_t(i);
+    }
+    const std::vector<uint32_t> lutc = uw::multi_code_table(f.lut, code_of);
+    if ((st = put(L.lutc, uw::kLutSize * 4, lutc.data())) != UW_OK) return st;
+  }
+  return UW_OK;
+}
+
+// Allocate the handle's device memory and copy the host streams into it.
+// With device_tables (load-time transcode) the palette tables, codes
+// included, are left for the caller's kernels to write.
+uw_status upload(uw_matrix* h, bool device_tables = false) {
+  const Layout L = layout_of(h);
+  if (hipMalloc(&h->dmem, L.total) != hipSuccess) {
+    h->dmem = nullptr;
+    return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", L.total);
+  }
+  h->dmem_bytes = L.total;
+  assign_pointers(h, L);
+  uint8_t* base = static_cast<uint8_t*>(h->dmem);
+  uw_status st = put_streams(h, L, device_tables, [&](size_t off, size_t bytes, const void* src) -> uw_status {
+    UW_HIP(hipMemcpy(base + off, src, bytes, hipMemcpyHostToDevice));
+    return UW_OK;
+  });
+  if (st != UW_OK) return st;
   UW_HIP(hipEventCreateWithFlags(&h->prep_done, hipEventDisableTiming));
   return UW_OK;
 }
@@ -937,8 +986,103 @@ uw_status uw_load(const char* path, uint32_t formats, uw_handle* out) {
   return UW_OK;
 }
 
+uw_status uw_upload(uw_handle h) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (!h->host_only) return UW_OK;
+  if (h->hf.sm.empty()) return fail(UW_ERR_UNSUPPORTED, "the handle holds no host streams");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(UW_ERR_NO_DEVICE, "no HIP device");
+  const Layout L = layout_of(h);
+  if (!h->pinned) {
+    // the first upload lays the streams out as on the device, in page-locked
+    // memory: every upload is then one DMA of the compressed bytes
+    if (hipHostMalloc(&h->pinned, L.total, hipHostMallocDefault) != hipSuccess) {
+      h->pinned = nullptr;
+      return fail(UW_ERR_OOM, "page-locked host allocation of %zu bytes failed", L.total);
+    }
+    h->pinned_bytes = L.total;
+    uint8_t* img = static_cast<uint8_t*>(h->pinned);
+    (void)put_streams(h, L, false, [&](size_t off, size_t bytes, const void* src) -> uw_status {
+      std::memcpy(img + off, src, bytes);
+      return UW_OK;
+    });
+  }
+  auto undo = [&](uw_status st) {
+    if (h->dmem) (void)hipFree(h->dmem);
+    if (h->prep_done) (void)hipEventDestroy(h->prep_done);
+    h->dmem = nullptr;
+    h->prep_done = nullptr;
+    return st;
+  };
+  if (hipMalloc(&h->dmem, L.total) != hipSuccess) {
+    h->dmem = nullptr;
+    return fail(UW_ERR_OOM, "device allocation of %zu bytes failed", L.total);
+  }
+  h->dmem_bytes = L.total;
+  assign_pointers(h, L);
+  if (hipMemcpyAsync(h->dmem, h->pinned, L.total, hipMemcpyHostToDevice, h->main) != hipSuccess)
+    return undo(fail(UW_ERR_HIP, "host-to-device copy failed"));
+  if (hipEventCreateWithFlags(&h->prep_done, hipEventDisableTiming) != hipSuccess)
+    return undo(fail(UW_ERR_HIP, "event creation failed"));
+  h->host_only = false;
+  h->keep_host = true;
+  return UW_OK;
+}
+
+uw_status uw_evict(uw_handle h) {
+  if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
+  if (h->host_only) return UW_OK;
+  if (!h->keep_host) return fail(UW_ERR_UNSUPPORTED, "the handle has no host copy (encode with UW_ENC_HOST_ONLY, then uw_upload)");
+  UW_HIP(hipStreamSynchronize(h->main));
+  if (h->side != h->main) UW_HIP(hipStreamSynchronize(h->side));
+  if (h->scratch && h->own_scratch) {
+    scratch_forget(h->scratch);
+    (void)hipFree(h->scratch);
+  }
+  h->scratch = nullptr;
+  h->scratch_cap = 0;
+  h->own_scratch = false;
+  h->prep_pipeline = 0;
+  if (h->prep_done) (void)hipEventDestroy(h->prep_done);
+  h->prep_done = nullptr;
+  (void)hipFree(h->dmem);
+  h->dmem = nullptr;
+  h->dmem_bytes = 0;
+  h->d_sm = h->d_nib = h->d_side = nullptr;
+  h->d_meta = nullptr;
+  h->d_words = h->d_offsets = h->d_lut = h->d_lut_codes = nullptr;
+  h->host_only = true;
+  return UW_OK;
+}
+
+uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t* x_dev, const int64_t* row_offsets,
+                            float* y_dev, int pipeline) {
+  if (!experts || n < 1 || !row_offsets || !x_dev || !y_dev) return fail(UW_ERR_INVALID_ARG, "null or empty argument");
+  if (row_offsets[0] != 0) return fail(UW_ERR_INVALID_ARG, "row_offsets[0] must be 0");
+  for (int32_t e = 0; e < n; ++e) {
+    if (!experts[e]) return fail(UW_ERR_INVALID_ARG, "null expert %d", e);
+    if (experts[e]->rows != experts[0]->rows || experts[e]->cols != experts[0]->cols)
+      return fail(UW_ERR_SHAPE, "expert %d has another shape than expert 0", e);
+    if (row_offsets[e + 1] < row_offsets[e]) return fail(UW_ERR_INVALID_ARG, "row_offsets decrease at %d", e);
+  }
+  for (int32_t e = 0; e < n; ++e)
+    if (experts[e]->host_only) return fail(UW_ERR_UNSUPPORTED, "expert %d is not on the device", e);
+  const int64_t rows = experts[0]->rows, cols = experts[0]->cols;
+  for (int32_t e = 0; e < n; ++e) {
+    const int64_t t = row_offsets[e + 1] - row_offsets[e];
+    if (t == 0) continue;
+    uw_status st = matmul_impl(experts[e], x_dev + row_offsets[e] * cols, y_dev + row_offsets[e] * rows, t, pipeline);
+    if (st != UW_OK) return st;
+  }
+  return UW_OK;
+}
+
 void uw_free(uw_handle h) {
   if (!h) return;
+  if (h->pinned) {
+    if (!h->host_only) (void)hipDeviceSynchronize();
+    (void)hipHostFree(h->pinned);
+  }
   if (!h->host_only) {
     (void)hipDeviceSynchronize();
     if (h->scratch && h->own_scratch) {

@@ -222,6 +222,38 @@ uw_status uw_save(uw_handle h, const char* path);
  * bytes after the end), UW_ERR_SHAPE, UW_ERR_OOM, UW_ERR_HIP. */
 uw_status uw_load(const char* path, uint32_t formats, uw_handle* out);
 
+/* Section 十一 (cold mixture-of-experts weights loaded on demand): make a
+ * host-only handle (uw_encode with UW_ENC_HOST_ONLY, or a host-only uw_load)
+ * usable on the current device: allocate its device memory and copy its
+ * compressed streams there -- the compressed bytes, not bf16, cross the host
+ * link (uw_info.resident_bytes of them).  The first call lays the streams out
+ * in page-locked host memory exactly as on the device (kept until uw_free, in
+ * addition to the host streams); each upload is then one asynchronous copy on
+ * the handle's main stream, which later work on that stream waits for, so an
+ * upload can overlap other streams' kernels.  uw_evict and a later uw_upload
+ * can repeat.  No-op for a handle already on the device.  Errors:
+ * UW_ERR_NO_DEVICE, UW_ERR_OOM, UW_ERR_HIP, UW_ERR_UNSUPPORTED (no host
+ * streams). */
+uw_status uw_upload(uw_handle h);
+
+/* Release the device copy of a handle made resident by uw_upload, after its
+ * streams have finished; it is host-only again (its scratch, if the library
+ * allocated it, is freed too).  No-op for a host-only handle;
+ * UW_ERR_UNSUPPORTED for a handle encoded on the device (no host copy). */
+uw_status uw_evict(uw_handle h);
+
+/* Mixture-of-experts form of uw_matmul: for each expert e < n, rows
+ * row_offsets[e] .. row_offsets[e+1]-1 of X (the tokens routed to e, grouped
+ * by expert by the caller) times expert e's W^T into the same rows of Y.
+ * x_dev: [row_offsets[n], cols] bf16, y_dev: [row_offsets[n], rows] fp32,
+ * row_offsets: host, n+1 non-decreasing entries from 0.  All experts share one
+ * shape and must be on the device; each expert's kernels go to its own main
+ * stream, in expert order; experts without rows are skipped.  Errors:
+ * UW_ERR_INVALID_ARG, UW_ERR_SHAPE (experts differ), UW_ERR_UNSUPPORTED (an
+ * expert is host-only or lacks the pipeline's format), as for uw_matmul. */
+uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t* x_dev, const int64_t* row_offsets,
+                            float* y_dev, int pipeline);
+
 void uw_free(uw_handle h);
 
 const char* uw_last_error(void);

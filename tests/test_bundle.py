@@ -123,3 +123,24 @@ def test_save_needs_huffman(tmp_path):
     m = uw.Matrix(CASES["tiny"](), uw.FMT_PALETTE | uw.ENC_HOST_ONLY)
     assert _status(lambda: m.save(str(tmp_path / "x.uwb"))) == uw.ERR_UNSUPPORTED
     assert not os.path.exists(tmp_path / "x.uwb")
+
+
+def test_upload_evict_grouped_host_checks():
+    """Host-side argument checks of the expert entry points (no device here)."""
+    w = CASES["tiny"]()
+    m = uw.Matrix(w, uw.FMT_PALETTE | uw.ENC_HOST_ONLY)
+    m.evict()  # host-only: nothing to release
+    m2 = uw.Matrix(synth.weights(256, 1024, 1, 0.001, 12), uw.FMT_PALETTE | uw.ENC_HOST_ONLY)
+    x = np.zeros((4, 512), dtype=np.uint16)
+    y = np.zeros((4, 256), dtype=np.float32)
+    assert _status(lambda: uw.grouped_matmul([m, m2], x, y, [0, 2, 4])) == uw.ERR_SHAPE
+    assert _status(lambda: uw.grouped_matmul([m, m], x, y, [0, 3, 2])) == uw.ERR_INVALID_ARG
+    assert _status(lambda: uw.grouped_matmul([m, m], x, y, [1, 2, 4])) == uw.ERR_INVALID_ARG
+    assert _status(lambda: uw.grouped_matmul([m, m], x, y, [0, 2, 4])) == uw.ERR_UNSUPPORTED
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if not has_gpu:
+        assert _status(m.upload) == uw.ERR_NO_DEVICE
