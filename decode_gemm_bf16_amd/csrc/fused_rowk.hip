@@ -125,11 +125,31 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
       rebuild_v2(st.s, v, w0, w1);
     }
     const uint32_t off = buf * xbuf + (uint32_t)lb * 128;
+    // B fragments read LA token blocks ahead of their MFMAs (left to itself
+    // the compiler reuses one register pair and waits on every read)
+    constexpr int LA = TB < 3 ? TB : 2;
+    u32x4 bq[LA + 1][2];
+    auto read_b = [&](u32x4 (&d)[2], int tb) {
+      const u32x4* px = (const u32x4*)(rowk_lds + xl[tb] + xm[tb] * off);
+      d[0] = px[0];
+      d[1] = px[1];
+    };
+#pragma unroll
+    for (int tb = 0; tb < LA; ++tb) read_b(bq[tb], tb);
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
-      const u32x4* px = (const u32x4*)(rowk_lds + xl[tb] + xm[tb] * off);
-      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(px[0]), acc[tb], 0, 0, 0);
-      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(px[1]), acc[tb], 0, 0, 0);
+      if (tb + LA < TB) read_b(bq[(tb + LA) % (LA + 1)], tb + LA);
+      const u32x4(&bc)[2] = bq[tb % (LA + 1)];
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(bc[0]), acc[tb], 0, 0, 0);
+      acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(bc[1]), acc[tb], 0, 0, 0);
+    }
+    // keep that order: the first LA blocks' reads, then per block two MFMAs
+    // and the reads of the block LA ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (tb + LA < TB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
   // activations of slice j: 16-byte pieces, S*8 per token
@@ -191,29 +211,39 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
     }
   }
 
-  // Epilogue: the P partial sums of each brick-row added in LDS, Y written
-  // in runs of R*16 consecutive rows per token.
-  f32x4* red = (f32x4*)rowk_lds;  // [wave][tb][lane]
+  // Epilogue: waves 1..P-1 of a brick-row hand their partial sums to wave 0
+  // through LDS (lane-major, no bank conflicts), wave 0 adds them and puts
+  // the brick-row's tile into an output tile [token][R*16 rows] (rows padded
+  // by 4), and Y is written from that in runs of R*16 consecutive rows.
+  constexpr int WR = R * 16, OROW = WR + 4;
+  f32x4* red = (f32x4*)rowk_lds;  // [rw][p-1][tb][lane]
+  float* out = (float*)(rowk_lds + (size_t)R * (P - 1) * TB * 64 * 16);
+  if (p > 0) {
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) red[(wave * TB + tb) * 64 + lane] = acc[tb];
+    for (int tb = 0; tb < TB; ++tb) red[((rw * (P - 1) + p - 1) * TB + tb) * 64 + lane] = acc[tb];
+  }
   __syncthreads();
-  constexpr int WR = R * 16;
+  if (p == 0) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      f32x4 sum = acc[tb];
+#pragma unroll
+      for (int pp = 1; pp < P; ++pp) sum += red[((rw * (P - 1) + pp - 1) * TB + tb) * 64 + lane];
+      // D layout: lane l holds rows 4*(l/16)+0..3 of column (token) l%16
+      *(f32x4*)&out[(tb * 16 + r) * OROW + rw * 16 + 4 * q] = sum;
+    }
+  }
+  __syncthreads();
   const int row0 = blockIdx.x * WR;
   const int nrow = min(WR, rows - row0);
-  const float* redf = (const float*)rowk_lds;
   for (int e = threadIdx.x; e < tokens * WR; e += NT) {
     const int tok = e / WR, rr = e - tok * WR;
     if (rr >= nrow) continue;
-    const int rw2 = rr >> 4, ri = rr & 15;
-    // D layout: lane l holds rows 4*(l/16)+0..3 of column (token) l%16
-    const int l = (ri >> 2) * 16 + (tok & 15), jj = ri & 3, tb = tok >> 4;
-    float sum = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < P; ++pp) sum += redf[(((rw2 * P + pp) * TB + tb) * 64 + l) * 4 + jj];
+    const float v = out[tok * OROW + rr];
     if (ksplit == 1)
-      y[(size_t)tok * rows + row0 + rr] = sum;
+      y[(size_t)tok * rows + row0 + rr] = v;
     else
-      unsafeAtomicAdd(y + (size_t)tok * rows + row0 + rr, sum);
+      unsafeAtomicAdd(y + (size_t)tok * rows + row0 + rr, v);
   }
 }
 
@@ -253,7 +283,8 @@ int rowk_tb(int64_t tokens) { return tokens <= 64 ? (int)((tokens + 15) / 16) : 
 size_t rowk_lds_bytes(int64_t tokens, int kper, int r, int p, int u) {
   const size_t xrow = (size_t)p * u * 128 + 16;
   const size_t in = 2 * (size_t)tokens * xrow + 32 + (size_t)r * kper * 8;
-  const size_t red = (size_t)r * p * rowk_tb(tokens) * 64 * 16;
+  // epilogue: the partial sums of waves 1..P-1 and the output tile
+  const size_t red = (size_t)r * (p - 1) * rowk_tb(tokens) * 64 * 16 + (size_t)rowk_tb(tokens) * 16 * (r * 16 + 4) * 4;
   return std::max(in, red);
 }
 
