@@ -37,7 +37,6 @@ struct RStage {
   u32x4 s[RB2][2];  // sign+mantissa runs, K pairs 0 and 1
   u32x4 e[RB2][2];  // exponent bytes (exponent form) or raw side-table bytes (zeros off raw rows)
   u32x2 n[RB2][2];  // 4-bit codes
-  uint32_t anyraw[RB2];
   bool raw[RB2];
 };
 
@@ -174,7 +173,6 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
         const uint32_t bfa = __builtin_amdgcn_readfirstlane(ma.y), bfb = __builtin_amdgcn_readfirstlane(mb.y);
         const uint32_t map = pb ? mapb : mapa;
         const uint32_t before = pb ? bfb : bfa;
-        w.anyraw[i] = mapa | mapb;
         w.raw[i] = (map >> r) & 1u;
         const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
         const uint32_t base = w.raw[i] ? (before + rank) * 64 + ks2 * 16 : kOffRange;
@@ -206,9 +204,7 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
   __builtin_amdgcn_s_waitcnt(0);  // every load of the prologue (the first tile included)
   __syncthreads();
 
-  // A fragments of a step: the branch-free rebuild (palette rows; the
-  // exponent form is all of it), then the rows of raw groups (rare, a
-  // wave-uniform branch)
+  // A fragments of a step
   auto rebuild = [&](const RStage<RB2, EXPM>& ws, bf16x8 (&an)[RB2][2][2]) {
 #pragma unroll
     for (int i = 0; i < RB2; ++i)
@@ -218,40 +214,31 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
         if (EXPM) {
           rebuild_exp2(ws.s[i][p], ws.e[i][p], a0, a1);
         } else {
+          // rows of raw groups take their exponents from the side table: a
+          // per-lane select, so the whole rebuild stays branch-free and can
+          // be interleaved with the MFMAs
           uint32_t v[4];
           palette_v(ws.n[i][p], lut, v);
+          const bool raw = ws.raw[i];
+          v[0] = raw ? rot_exp(ws.e[i][p].x) : v[0];
+          v[1] = raw ? rot_exp(ws.e[i][p].y) : v[1];
+          v[2] = raw ? rot_exp(ws.e[i][p].z) : v[2];
+          v[3] = raw ? rot_exp(ws.e[i][p].w) : v[3];
           rebuild_v2(ws.s[i][p], v, a0, a1);
         }
         an[i][p][0] = as_bf16x8(a0);
         an[i][p][1] = as_bf16x8(a1);
       }
   };
-  auto patch_raw = [&](const RStage<RB2, EXPM>& ws, bf16x8 (&an)[RB2][2][2]) {
-    if (EXPM) return;
-#pragma unroll
-    for (int i = 0; i < RB2; ++i)
-      if (ws.anyraw[i]) {
-        if (ws.raw[i]) {
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            u32x4 a0, a1;
-            rebuild_exp2(ws.s[i][p], ws.e[i][p], a0, a1);
-            an[i][p][0] = as_bf16x8(a0);
-            an[i][p][1] = as_bf16x8(a1);
-          }
-        }
-      }
-  };
 
   bf16x8 a[2][RB2][2][2];
   rebuild(w[0], a[0]);
-  patch_raw(w[0], a[0]);
   // One step: request the weights of step kb+D (into the stage step kb was
   // rebuilt from) and the tile of step kb+X-1; the MFMAs of step kb on a[C],
   // each followed by a few VALU ops of the rebuild of step kb+1 into a[C^1]
   // (one wave per SIMD: the VALU issues while the matrix core works); then
-  // the raw rows of step kb+1, the wait for this wave's part of tile kb+1
-  // and the barrier that publishes it.
+  // the wait for this wave's part of tile kb+1 and the barrier that
+  // publishes it.
   auto step = [&](RStage<RB2, EXPM>& wcur, const RStage<RB2, EXPM>& wnext, bf16x8 (&ac)[RB2][2][2],
                   bf16x8 (&an)[RB2][2][2], int kb) {
     load_w(wcur, kb + D, true);
@@ -285,7 +272,6 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // and an LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
-    patch_raw(wnext, an);
     // this wave's part of tile kb+1 (requested X-2 steps ago) has landed once
     // at most the loads of the X-2 later steps are outstanding
     wait_vmcnt<(X - 2) * (WL + XL)>();
