@@ -174,7 +174,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   // below do better.
   const int64_t rb8 = (brows + 7) / 8;
   if (kbn < 256) {
-    if (rb8 * ((tokens + 127) / 128) >= 192) return Variant{1, 0, 1, 0, 18};
+    const int64_t wg128 = rb8 * ((tokens + 127) / 128);
+    // (eight activation tiles in flight when one workgroup per CU suffices,
+    // three -- two or three workgroups per CU -- otherwise)
+    if (wg128 >= 192) return Variant{1, 0, 1, 0, wg128 <= 256 ? 20 : 18};
     if (rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, tokens <= 192 ? 13 : 16};
   }
   const int64_t tblk = (tokens + 127) / 128;
