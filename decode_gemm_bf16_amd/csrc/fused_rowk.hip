@@ -305,10 +305,16 @@ size_t rowk_plan(int64_t tokens, int64_t rows, int64_t cols, const Variant& v, i
   return rowk_lds_bytes(tokens, kper, R, P, U);
 }
 
+// shapes built for 65..128 tokens: {R, P, U, D}
+bool big_shape(const Variant& v) {
+  const int R = v.tile, P = v.waves, U = v.ksplit, D = v.unroll;
+  return (R == 4 && P == 4 && U == 1 && D == 2) || (R == 4 && P == 2 && U == 2 && D == 2);
+}
+
 bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v) {
   if (tokens < 1 || tokens > 128) return false;
-  // above 64 tokens only the R4 P4 U1 shape is built
-  if (tokens > 64 && !(v.tile == 4 && v.waves == 4 && v.ksplit == 1 && v.unroll == 2)) return false;
+  // above 64 tokens only the R4 P4 U1 and R4 P2 U2 shapes are built
+  if (tokens > 64 && !big_shape(v)) return false;
   return rowk_plan(tokens, rows, cols, v, nullptr, nullptr) <= kRowkLdsBytes;
 }
 
@@ -324,8 +330,14 @@ hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64
     if (e != hipSuccess) return e;
   }
   if (tokens > 64) {  // 65..128 tokens: 6 or 8 token blocks
-    if (tokens <= 96) return launch_rowk_t<4, 4, 1, 2, 6>(w, x, y, tokens, kper, ks, lds, s);
-    return launch_rowk_t<4, 4, 1, 2, 8>(w, x, y, tokens, kper, ks, lds, s);
+#define UW_BIG(RR, PP, UU, DD)                                                             \
+  if (R == RR && P == PP && U == UU && D == DD) {                                          \
+    if (tokens <= 96) return launch_rowk_t<RR, PP, UU, DD, 6>(w, x, y, tokens, kper, ks, lds, s); \
+    return launch_rowk_t<RR, PP, UU, DD, 8>(w, x, y, tokens, kper, ks, lds, s);            \
+  }
+    UW_BIG(4, 4, 1, 2) UW_BIG(4, 2, 2, 2)
+#undef UW_BIG
+    return hipErrorInvalidValue;
   }
 #define UW_CASE(RR, PP, UU, DD) \
   if (R == RR && P == PP && U == UU && D == DD)  \

@@ -80,7 +80,7 @@ const Named kLarge[] = {
     {{1, 0, 1, 0, 20}, "large:t20(4x32r x128t,32x32,ring d4 x8 b4)"},
     {{1, 0, 1, 0, 21}, "large:t21(4x64r x128t,32x32,ring d2 x3 b2)"},
     // whole K per workgroup, 16x16x32 instructions, up to 128 tokens
-    {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},
+    {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},   {{4, 2, 2, 2, 4}, "rowk:r4p2u2d2"},
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -160,9 +160,9 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     if (tokens >= 16) return Variant{3, 8, 1, 2, 0};
     return small_default(tokens, rows, cols);
   }
-  // up to 128 tokens: the whole-K kernel (16x16x32 instructions, four waves
-  // per SIMD, activations streamed through LDS in 4-brick slices)
-  const Variant rowk{4, 4, 1, 2, 4};
+  // up to 128 tokens: the whole-K kernel (16x16x32 instructions, two waves
+  // per brick-row, activations streamed through LDS in 4-brick slices)
+  const Variant rowk{4, 2, 2, 2, 4};
   if (tokens <= 128 && rowk_fits(tokens, rows, cols, rowk)) return rowk;
   // 256 x 256 tiles with the rebuild interleaved into the MFMAs once there are
   // enough tokens to fill the chip with them (one workgroup per CU)
