@@ -278,7 +278,9 @@ hipError_t launch_rowk_c(const FusedW& w, const uint16_t* x, float* y, int64_t t
 }  // namespace
 
 // token blocks of 16 the kernel is instantiated with for `tokens`
-int rowk_tb(int64_t tokens) { return tokens <= 64 ? (int)((tokens + 15) / 16) : tokens <= 96 ? 6 : 8; }
+int rowk_tb(int64_t tokens) {
+  return tokens <= 64 ? (int)((tokens + 15) / 16) : tokens <= 96 ? 6 : tokens <= 128 ? 8 : tokens <= 192 ? 12 : 16;
+}
 
 size_t rowk_lds_bytes(int64_t tokens, int kper, int r, int p, int u) {
   const size_t xrow = (size_t)p * u * 128 + 16;
@@ -297,7 +299,7 @@ size_t rowk_plan(int64_t tokens, int64_t rows, int64_t cols, const Variant& v, i
   const int kbn = (int)(cols / 64);
   const int64_t groups = (rows / 16 + R - 1) / R;
   int ks = 1;
-  if (groups < 128) ks = (int)std::max<int64_t>(1, std::min<int64_t>(256 / groups, kbn / (2 * S)));
+  if (groups <= 128) ks = (int)std::max<int64_t>(1, std::min<int64_t>(256 / groups, kbn / (2 * S)));
   const int kper = ((kbn + ks - 1) / ks + S - 1) / S * S;
   ks = (kbn + kper - 1) / kper;
   if (kper_out) *kper_out = kper;
@@ -311,10 +313,15 @@ bool big_shape(const Variant& v) {
   return (R == 4 && P == 4 && U == 1 && D == 2) || (R == 4 && P == 2 && U == 2 && D == 2);
 }
 
+// shape built for 129..256 tokens: 2-brick slices, whose activations still
+// fit LDS twice
+bool huge_shape(const Variant& v) { return v.tile == 4 && v.waves == 2 && v.ksplit == 1 && v.unroll == 2; }
+
 bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v) {
-  if (tokens < 1 || tokens > 128) return false;
+  if (tokens < 1 || tokens > 256) return false;
+  if (tokens > 128 && !huge_shape(v)) return false;
   // above 64 tokens only the R4 P4 U1 and R4 P2 U2 shapes are built
-  if (tokens > 64 && !big_shape(v)) return false;
+  if (tokens > 64 && tokens <= 128 && !big_shape(v)) return false;
   return rowk_plan(tokens, rows, cols, v, nullptr, nullptr) <= kRowkLdsBytes;
 }
 
@@ -328,6 +335,10 @@ hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64
   if (ks > 1) {
     hipError_t e = launch_zero(y, tokens * w.rows, s);
     if (e != hipSuccess) return e;
+  }
+  if (tokens > 128) {  // 129..256 tokens: 12 or 16 token blocks
+    if (tokens <= 192) return launch_rowk_t<4, 2, 1, 2, 12>(w, x, y, tokens, kper, ks, lds, s);
+    return launch_rowk_t<4, 2, 1, 2, 16>(w, x, y, tokens, kper, ks, lds, s);
   }
   if (tokens > 64) {  // 65..128 tokens: 6 or 8 token blocks
 #define UW_BIG(RR, PP, UU, DD)                                                             \

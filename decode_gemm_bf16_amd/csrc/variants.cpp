@@ -81,6 +81,7 @@ const Named kLarge[] = {
     {{1, 0, 1, 0, 21}, "large:t21(4x64r x128t,32x32,ring d2 x3 b2)"},
     // whole K per workgroup, 16x16x32 instructions, up to 128 tokens
     {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},   {{4, 2, 2, 2, 4}, "rowk:r4p2u2d2"},
+    {{4, 2, 1, 2, 4}, "rowk:r4p2u1d2"},   // up to 256 tokens
 };
 constexpr int kNSmall = sizeof(kSmall) / sizeof(kSmall[0]);
 constexpr int kNLarge = sizeof(kLarge) / sizeof(kLarge[0]);
@@ -180,6 +181,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     if (wg128 >= 192) return Variant{1, 0, 1, 0, wg128 <= 256 ? 20 : 18};
     if (rb8 * ((tokens + 63) / 64) >= 192) return Variant{1, 0, 1, 0, tokens <= 192 ? 13 : 16};
   }
+  // up to 256 tokens on matrices the deep-prefetch tiles do not fill: the
+  // whole-K kernel with 2-brick slices (K split for short matrices)
+  const Variant rowk256{4, 2, 1, 2, 4};
+  if (tokens <= 256 && rowk_fits(tokens, rows, cols, rowk256)) return rowk256;
   const int64_t tblk = (tokens + 127) / 128;
   const int64_t wg0 = ((brows + 15) / 16) * tblk;  // tile 0: 256 rows per workgroup
   const int64_t wg1 = ((brows + 7) / 8) * tblk;    // tiles 1/5: 128 rows per workgroup
