@@ -59,13 +59,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_label(name: str, tokens: int) -> str:
+def kernel_label(name: str, tokens: int, max_row_raw: int = 0) -> str:
     """The name rocprofv3 gives (template arguments included) to the fused
-    kernel that a small-batch variant launches."""
+    kernel that a small-batch variant launches (the gemv kernel keeps the raw
+    groups' bytes in LDS when no brick-row has more than 256 raw groups)."""
     import re
     m = re.match(r"gemv:w(\d+):d(\d+)", name)
     if m:
-        return f"fused_gemv_kernel<{m[1]}, {m[2]}>"
+        return f"fused_gemv_kernel<{m[1]}, {m[2]}, {'true' if max_row_raw <= 256 else 'false'}>"
     m = re.match(r"small:w(\d+):k\d+:u(\d+)", name)
     if m:
         return f"fused_small_kernel<{m[1]}, {min(4, (tokens + 15) // 16)}, false, {m[2]}>"
@@ -569,7 +570,7 @@ def main() -> int:
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
             "algorithmic_bytes_per_launch": int(algo_bytes), "avg_launch_us": round(ms * 1e3, 3),
-            "kernel": kernel_label(in_use, tokens), "kernel_sha": kernel_sha(),
+            "kernel": kernel_label(in_use, tokens, pinfo["max_row_raw"]), "kernel_sha": kernel_sha(),
         },
         "extra": {
             "tflops": round(2.0 * n * tokens / t_s / 1e12, 4),

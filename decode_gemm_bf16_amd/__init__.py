@@ -45,7 +45,7 @@ class Info(C.Structure):
         ("code_lengths", C.c_uint8 * 256), ("raw_groups", C.c_uint64), ("groups", C.c_uint64),
         ("stream_bits", C.c_uint64), ("stream_words", C.c_uint64), ("bpw_palette", C.c_double),
         ("bpw_huffman", C.c_double), ("bpw_resident", C.c_double), ("resident_bytes", C.c_uint64),
-        ("scratch_bytes", C.c_uint64 * 5),
+        ("scratch_bytes", C.c_uint64 * 5), ("max_row_raw", C.c_uint32),
     ]
 
 

@@ -109,6 +109,16 @@ double HostFormat::bpw_huffman() const {
   return bits / double(n());
 }
 
+uint32_t max_row_raw(const uint32_t* rawmap, const uint32_t* rawbefore, uint64_t bricks, uint64_t kbn) {
+  uint32_t best = 0;
+  for (uint64_t b0 = 0; b0 + kbn <= bricks; b0 += kbn) {
+    const uint64_t last = b0 + kbn - 1;
+    const uint32_t n = rawbefore[last] + uint32_t(__builtin_popcount(rawmap[last])) - rawbefore[b0];
+    if (n > best) best = n;
+  }
+  return best;
+}
+
 std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t formats, HostFormat& f) {
   if (!w) return "null weight pointer";
   if (rows <= 0 || cols <= 0 || rows % kBrickRows || cols % kBrickCols)
@@ -178,6 +188,7 @@ std::string encode_host(const uint16_t* w, int64_t rows, int64_t cols, uint32_t 
       }
     }
     if (seen > 0xFFFFFFFFull) return "too many raw groups";
+    f.max_row_raw = max_row_raw(f.rawmap.data(), f.rawbefore.data(), nb, uint64_t(cols) / 64);
     f.n_raw = seen;
   }
 

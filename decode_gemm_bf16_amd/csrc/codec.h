@@ -34,6 +34,7 @@ struct HostFormat {
   std::vector<uint32_t> rawbefore;  // per brick: raw groups in earlier bricks
   std::vector<uint8_t> side;        // 64 original exponents per raw group
   uint64_t n_raw = 0;
+  uint32_t max_row_raw = 0xFFFFFFFFu;  // most raw groups in one brick-row (16 rows); unknown: all ones
 
   // Huffman form
   uint8_t lengths[256] = {};
@@ -48,6 +49,10 @@ struct HostFormat {
   double bpw_palette() const;
   double bpw_huffman() const;
 };
+
+// Most raw groups in one brick-row (kbn consecutive bricks) from the per-brick
+// raw maps and raw-groups-before counts.
+uint32_t max_row_raw(const uint32_t* rawmap, const uint32_t* rawbefore, uint64_t bricks, uint64_t kbn);
 
 // Returns an empty string on success, else the reason.  `formats` uses the
 // UW_FMT_* flags of uw.h (palette tables are built for PALETTE or RAWAUX).

@@ -183,25 +183,28 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
 
 // Few tokens whose activations fit in LDS (tokens x cols <= kGemvX): the same
 // brick-row-per-workgroup split, arranged so that each wave keeps only weight
-// bytes in its load pipeline.  At the start the workgroup copies x and its
-// brick-row's per-brick table into LDS (all loads issued before the one wait),
-// so a brick costs three buffer loads: sign+mantissa, codes and the raw
-// side-table bytes (lanes of rows that are not raw read past the buffer's end,
-// which returns zeros without touching memory; issuing the load on every
-// brick keeps the load count per stage fixed, so waits cover one stage only).
-// Each wave runs a ring of D stages; the B operand comes from LDS at compute
-// time; partial sums are reduced one output per thread.
+// bytes in its load pipeline.  At the start the workgroup copies x, its
+// brick-row's per-brick table and the raw groups' side-table bytes of the
+// brick-row (one contiguous range: raw groups are numbered in brick order)
+// into LDS, all loads issued before the one wait, so a brick costs two buffer
+// loads: sign+mantissa and codes.  A matrix with a brick-row of more raw
+// groups than the LDS copy holds (kGemvSideCap; a quarter of the groups at
+// 4096 columns) runs the SIDE_LDS = false form, which reads raw groups' bytes
+// from global memory when it meets them instead.  Each
+// wave runs a ring of D stages; the B operand comes from LDS at compute time;
+// partial sums are reduced one output per thread.
 constexpr int kGemvX = (int)kGemvXElems;   // bf16 elements of x held in LDS
 constexpr int kGemvKbn = (int)kGemvKbnMax;  // brick columns whose table fits the LDS copy
+constexpr int kGemvSideCap = 256;           // raw groups per brick-row whose bytes fit the LDS copy
 
 struct GStage {
-  u32x4 s;       // sign+mantissa bytes
-  u32x4 e;       // raw side-table bytes (zeros for rows that are not raw)
-  u32x2 n;       // 4-bit codes
-  uint32_t map;  // wave-uniform raw-row map of the brick
+  u32x4 s;          // sign+mantissa bytes
+  u32x2 n;          // 4-bit codes
+  uint32_t map;     // wave-uniform raw-row map of the brick
+  uint32_t before;  // wave-uniform raw groups before the brick
 };
 
-template <int WAVES, int D>
+template <int WAVES, int D, bool SIDE_LDS>
 __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
@@ -222,10 +225,12 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
   const uint32_t clane = code_lane_off(q, r, 8, codes_ilv);
   const bool live = r < tokens;
   // LDS: x (tokens x cols bf16), a 32-byte zero tail read by lanes of absent
-  // tokens, then the brick-row's per-brick table
+  // tokens, the brick-row's per-brick table, then (16-byte aligned) the
+  // brick-row's raw-group bytes
   extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
   const uint32_t xbytes = (uint32_t)tokens * cols * 2;
   uint2* ms = (uint2*)(gemv_lds + xbytes + 32);
+  const uint8_t* sl = gemv_lds + ((xbytes + 32 + (uint32_t)kbn * 8 + 15) & ~15u);
   const uint32_t xl_lane = live ? ((uint32_t)r * cols + q * 16) * 2 : xbytes;
   const uint32_t xl_step = live ? 128u : 0u;
 
@@ -234,48 +239,30 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     i = min(i, nmine - 1);  // a stage past the end re-reads the last brick; compute skips it
     const int kb = wave + WAVES * i;
     const uint2 m = table_in_lds ? ms[kb] : meta[brick_row0 + kb];
-    const uint32_t map = __builtin_amdgcn_readfirstlane(m.x);
-    const uint32_t before = __builtin_amdgcn_readfirstlane(m.y);
+    st.map = __builtin_amdgcn_readfirstlane(m.x);
+    st.before = __builtin_amdgcn_readfirstlane(m.y);
     const uint32_t b = brick_row0 + kb;
     st.s = ld16s(rs_sm, lane16, b * 1024);
     st.n = ld8s(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
-    st.map = map;
-    const bool raw = (map >> r) & 1u;
-    const uint32_t rank = __builtin_popcount(map & ((1u << r) - 1u));
-    st.e = ld16(rs_side, raw ? (before + rank) * 64 + q * 16 : kOffRange, 0);
   };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const GStage& st, int i) {
-    const int kb = wave + WAVES * i;
-    const u32x4* p = (const u32x4*)(gemv_lds + xl_lane + kb * xl_step);
-    const u32x4 xb0 = p[0], xb1 = p[1];
-    uint32_t v[4];
-    palette_v(st.n, lut, v);
-    if (st.map) {  // wave-uniform: the brick holds a raw group
-      if ((st.map >> r) & 1u) {
-        v[0] = rot_exp(st.e.x);
-        v[1] = rot_exp(st.e.y);
-        v[2] = rot_exp(st.e.z);
-        v[3] = rot_exp(st.e.w);
-      }
-    }
-    u32x4 w0, w1;
-    rebuild_v2(st.s, v, w0, w1);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(xb0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(xb1), acc, 0, 0, 0);
-  };
-
   GStage st[D];
   if (nmine > 0) {  // the first stages read the table from global memory (scalar loads)
 #pragma unroll
     for (int j = 0; j < D; ++j) fetch(st[j], j, false);
   }
+  // the brick-row's raw groups: raw0 .. raw0 + nraw - 1
+  const uint2 m_first = meta[brick_row0], m_last = meta[brick_row0 + kbn - 1];
+  const uint32_t raw0 = __builtin_amdgcn_readfirstlane(m_first.y);
+  const uint32_t nraw = __builtin_amdgcn_readfirstlane(m_last.y) +
+                        __builtin_popcount(__builtin_amdgcn_readfirstlane(m_last.x)) - raw0;
   {
     constexpr int NT = WAVES * 64;
     constexpr int NXV = (kGemvX / 8 + NT - 1) / NT, NMV = (kGemvKbn + NT - 1) / NT;
+    constexpr int NSV = SIDE_LDS ? (kGemvSideCap * 4 + NT - 1) / NT : 0;
     const rsrc_t rs_meta = make_rsrc(meta + brick_row0, (uint64_t)kbn * 8);
     const int n16 = tokens * cols / 8;
-    u32x4 xv[NXV];
+    const uint32_t n16s = SIDE_LDS ? nraw * 4 : 0u;  // 16-byte pieces of the raw-group bytes
+    u32x4 xv[NXV], sv[NSV > 0 ? NSV : 1];
     u32x2 mv[NMV];
 #pragma unroll
     for (int k = 0; k < NMV; ++k) {
@@ -288,6 +275,11 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
       xv[k] = ld16(rs_x, i < n16 ? i * 16 : kOffRange, 0);
     }
 #pragma unroll
+    for (int k = 0; k < NSV; ++k) {
+      const uint32_t i = threadIdx.x + k * NT;
+      sv[k] = ld16(rs_side, i < n16s ? raw0 * 64 + i * 16 : kOffRange, 0);
+    }
+#pragma unroll
     for (int k = 0; k < NMV; ++k) {
       const int i = threadIdx.x + k * NT;
       if (i < kbn) ms[i] = uint2{mv[k].x, mv[k].y};
@@ -297,9 +289,41 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
       const int i = threadIdx.x + k * NT;
       if (i < n16) ((u32x4*)gemv_lds)[i] = xv[k];
     }
+#pragma unroll
+    for (int k = 0; k < NSV; ++k) {
+      const uint32_t i = threadIdx.x + k * NT;
+      if (i < n16s) ((u32x4*)sl)[i] = sv[k];
+    }
     if (threadIdx.x < 2) ((u32x4*)(gemv_lds + xbytes))[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
   }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const GStage& st, int i) {
+    const int kb = wave + WAVES * i;
+    const u32x4* p = (const u32x4*)(gemv_lds + xl_lane + kb * xl_step);
+    const u32x4 xb0 = p[0], xb1 = p[1];
+    uint32_t v[4];
+    palette_v(st.n, lut, v);
+    if (st.map) {  // wave-uniform: the brick holds a raw group
+      if ((st.map >> r) & 1u) {
+        const uint32_t g = st.before + __builtin_popcount(st.map & ((1u << r) - 1u));  // this row's raw group
+        u32x4 e;
+        if constexpr (SIDE_LDS) {
+          e = *(const u32x4*)(sl + (g - raw0) * 64 + q * 16);
+        } else {
+          e = ld16(rs_side, g * 64 + q * 16, 0);
+        }
+        v[0] = rot_exp(e.x);
+        v[1] = rot_exp(e.y);
+        v[2] = rot_exp(e.z);
+        v[3] = rot_exp(e.w);
+      }
+    }
+    u32x4 w0, w1;
+    rebuild_v2(st.s, v, w0, w1);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(xb0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(xb1), acc, 0, 0, 0);
+  };
   for (int i = 0; i < nmine; i += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
@@ -325,10 +349,17 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
 
 template <int WAVES, int D>
 hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, hipStream_t s) {
-  const size_t lds = (size_t)tokens * w.cols * 2 + 32 + (size_t)(w.cols / 64) * 8;
-  hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s, w.sm,
-                     w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
-                     (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
+  const size_t head = (size_t)tokens * w.cols * 2 + 32 + (size_t)(w.cols / 64) * 8;
+  const bool side_lds = w.max_row_raw <= (uint32_t)kGemvSideCap;
+  const size_t lds = side_lds ? ((head + 15) & ~(size_t)15) + (size_t)kGemvSideCap * 64 : head;
+  if (side_lds)
+    hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D, true>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s,
+                       w.sm, w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
+                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
+  else
+    hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D, false>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s,
+                       w.sm, w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
+                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
   return hipGetLastError();
 }
 
@@ -365,7 +396,7 @@ hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64
     return hipErrorInvalidValue;
 #define UW_CASE(W, D) \
   if (v.waves == W && v.unroll == D) return launch_gemv<W, D>(w, x, y, tokens, s);
-  UW_CASE(8, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)
+  UW_CASE(8, 2) UW_CASE(8, 1) UW_CASE(4, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)
 #undef UW_CASE
   return hipErrorInvalidValue;
 }

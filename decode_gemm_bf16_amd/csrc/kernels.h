@@ -19,6 +19,7 @@ struct FusedW {
   bool exp_mode;           // codes are exponent bytes (pipeline 2)
   bool codes_ilv;          // codes are in the interleaved scratch order (pipelines 2, 3; see recon.h)
   uint64_t codes_bytes;    // size of the codes buffer
+  uint32_t max_row_raw;    // palette mode: most raw groups in one brick-row (all ones: unknown)
 };
 
 // Fused-kernel variants.  Small-batch kernels (tokens <= 64): one workgroup per

@@ -187,6 +187,7 @@ uw::FusedW fused_view(const uw_matrix* h, bool exp_mode, const uint8_t* codes) {
   f.meta = h->d_meta;
   f.side = h->d_side;
   f.side_bytes = std::max<uint64_t>(h->hf.n_raw * 64, 64);
+  f.max_row_raw = h->hf.max_row_raw;
   for (int i = 0; i < 4; ++i) f.lut[i] = h->lut_v[i];
   f.rows = h->rows;
   f.cols = h->cols;
@@ -549,6 +550,16 @@ uw_status transcode_upload(uw_matrix* h) {
   UW_HIP(uw::launch_palette_pack(exps, nb, cof, rawmap, wg_before, h->d_meta,
                                  h->has(UW_FMT_PALETTE) ? h->d_nib : nullptr, h->d_side, nullptr));
   UW_HIP(hipDeviceSynchronize());
+  {  // the largest brick-row raw count, from the table just built
+    std::vector<uint2> meta(nb);
+    UW_HIP(hipMemcpy(meta.data(), h->d_meta, nb * 8, hipMemcpyDeviceToHost));
+    std::vector<uint32_t> map(nb), before(nb);
+    for (uint64_t b = 0; b < nb; ++b) {
+      map[b] = meta[b].x;
+      before[b] = meta[b].y;
+    }
+    f.max_row_raw = uw::max_row_raw(map.data(), before.data(), nb, uint64_t(h->cols) / 64);
+  }
   return UW_OK;
 }
 
@@ -784,6 +795,7 @@ uw_status uw_query(uw_handle h, uw_info* o) {
   std::memcpy(o->palette, f.palette, 16);
   std::memcpy(o->code_lengths, f.lengths, 256);
   o->raw_groups = f.n_raw;
+  o->max_row_raw = h->has_pal_tables() ? f.max_row_raw : 0xFFFFFFFFu;
   o->groups = f.n() / 64;
   o->stream_bits = f.stream_bits;
   o->stream_words = (f.stream_bits + 31) / 32;
@@ -873,6 +885,7 @@ uw_status uw_clone(uw_handle h, uw_handle* out) {
   c->hf.distinct = h->hf.distinct;
   std::memcpy(c->hf.palette, h->hf.palette, 16);
   c->hf.n_raw = h->hf.n_raw;
+  c->hf.max_row_raw = h->hf.max_row_raw;
   std::memcpy(c->hf.lengths, h->hf.lengths, 256);
   std::memcpy(c->hf.codes, h->hf.codes, sizeof c->hf.codes);
   c->hf.stream_bits = h->hf.stream_bits;

@@ -38,6 +38,7 @@ const Named kSmall[] = {
     // x held in LDS (palette forms, tokens x cols <= 16384); {waves, ring depth}
     {{2, 8, 1, 2, 0}, "gemv:w8:d2"},      {{2, 16, 1, 2, 0}, "gemv:w16:d2"},
     {{2, 8, 1, 3, 0}, "gemv:w8:d3"},      {{2, 4, 1, 3, 0}, "gemv:w4:d3"},
+    {{2, 8, 1, 1, 0}, "gemv:w8:d1"},      {{2, 4, 1, 2, 0}, "gemv:w4:d2"},
     // a K slice of x in LDS shared by `waves` brick-rows; {waves, ring depth}
     {{3, 16, 1, 2, 0}, "mid:w16:d2"},     {{3, 8, 1, 2, 0}, "mid:w8:d2"},
     {{3, 16, 1, 3, 0}, "mid:w16:d3"},     {{3, 4, 1, 2, 0}, "mid:w4:d2"},
@@ -146,7 +147,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // activations in LDS when they fit and there are enough brick-rows to
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
-    if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128) return Variant{2, 8, 1, 2, 0};
+    // (one stage in flight per wave when the brick-rows alone fill the chip,
+    // three for fewer, longer brick-rows)
+    if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128)
+      return brows >= 512 ? Variant{2, 8, 1, 1, 0} : Variant{2, 8, 1, 3, 0};
     // from 12 tokens (20 for matrices too short to fill the chip without a
     // K split): four brick-rows per workgroup over the whole of K, the
     // activations streamed through LDS in 8-brick slices

@@ -113,6 +113,8 @@ typedef struct {
   double bpw_resident;         /* bits/weight of what this handle stores        */
   uint64_t resident_bytes;     /* compressed bytes held on the device           */
   uint64_t scratch_bytes[5];   /* scratch that pipeline p (1..4) needs          */
+  uint32_t max_row_raw;        /* most raw groups in one brick-row of 16 rows   */
+                               /* (0xFFFFFFFF: no palette tables)               */
 } uw_info;
 
 /* Encode a bf16 matrix (section 四): split each weight into its exponent and

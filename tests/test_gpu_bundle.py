@@ -56,6 +56,11 @@ def test_transcoded_streams_byte_equal(env, tmp_path, name):
     assert np.array_equal(m.export(uw.STREAM_SIDE), want["side"])
     assert np.array_equal(m.export(uw.STREAM_SM), want["sm"])
     assert m.info()["raw_groups"] == want["n_raw"]
+    # the largest brick-row raw count, from the oracle's tables
+    kbn = w.shape[1] // 64
+    rm, rb = want["brick_rawmap"], want["brick_rawbefore"]
+    counts = [int(rb[b + kbn - 1]) + bin(int(rm[b + kbn - 1])).count("1") - int(rb[b]) for b in range(0, len(rm), kbn)]
+    assert m.info()["max_row_raw"] == max(counts)
     # the palette-only handle decodes through the transcoded tables
     m2 = uw.Matrix.load(str(p), uw.FMT_PALETTE)
     out = torch.empty(w.shape, dtype=torch.int16, device="cuda")

@@ -183,6 +183,60 @@ def test_rowk_fewer_bricks_than_waves(env, tokens):
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
 
 
+def _raw_heavy_weights():
+    """4 brick-rows x 4096 columns (1024 groups of 64 per brick-row) with raw
+    groups forced by one exponent outside the palette per group (exponents
+    20..107 spread so that none enters the palette 108..123): brick-row 0 holds 257 raw
+    groups, 1 all 1024, 2 none added, 3 exactly 256 (16 whole bricks)."""
+    w = synth.weights(64, 4096, 31, 0.0, 12).copy()
+    e = np.clip((w >> 7) & 0xFF, 108, 123)  # every exponent in one 16-value palette: no other raw group
+    w = ((w & 0x807F) | (e << 7)).astype(np.uint16)
+
+    def force_raw(row, col, k):
+        e = 20 + k % 88
+        w[row, col] = (w[row, col] & 0x807F) | (e << 7)
+
+    k = 0
+    for g in range(257):  # brick-row 0: bricks 0..16, rows 0..15 (257 = 16 * 16 + 1)
+        kb, r = divmod(g, 16)
+        force_raw(r, kb * 64 + 5, k); k += 1
+    for r in range(16):
+        for kb in range(64):
+            force_raw(16 + r, kb * 64 + (r * 7 + kb) % 64, k); k += 1
+    for r in range(16):
+        for kb in range(16):
+            force_raw(48 + r, kb * 64 + 63, k); k += 1
+    return w
+
+
+@pytest.mark.parametrize("tokens", [1, 3, 16])
+def test_gemv_raw_heavy_brick_rows(env, tokens):
+    """The LDS-held activations kernel copies each brick-row's raw-group bytes
+    into LDS when no brick-row has more than 256 raw groups (brick-rows 2-3:
+    0 and exactly 256), and reads them from global memory otherwise (all four
+    brick-rows: 257 and 1024 as well); every gemv variant, direct palette and
+    runtime transcode, against fp64 per brick-row."""
+    torch, uw = env
+    w_all = _raw_heavy_weights()
+    x = synth.activations(tokens, 4096, xseed=7)
+    names = uw.variants(tokens)
+    picked = [v for v, n in enumerate(names) if n.startswith("gemv")]
+    assert len(picked) >= 6
+    for w, raw in ((w_all, 257 + 1024 + 256), (np.ascontiguousarray(w_all[32:]), 256)):
+        m = _both(env, w)
+        assert m.info()["raw_groups"] == raw
+        ref = oracle.matmul_fp64(x, w)
+        for v in picked:
+            for p in (3, 4):
+                y = _run(env, m, x, p, variant=v)
+                assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
+                # per brick-row as well, so that a wrong group in one
+                # brick-row cannot hide behind the magnitude of another
+                for br in range(w.shape[0] // 16):
+                    sl = slice(16 * br, 16 * br + 16)
+                    assert oracle.rel_err(y[:, sl], ref[:, sl]) <= TOL, (names[v], p, br)
+
+
 @pytest.mark.parametrize("rows,cols", [(1024, 4096), (3584, 18944), (128256, 4096)])
 def test_other_projection_shapes(env, rows, cols):
     """Attention k/v (1024 x 4096), a wider MLP's down projection

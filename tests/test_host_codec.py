@@ -136,7 +136,10 @@ def test_variant_in_use_resolution():
     built-in rule, the exponent-form fallback of the LDS-activation shapes,
     an explicit variant and a plan."""
     m = uw.Matrix(synth.weights(2048, 4096, 1, 0.0005, 10), HOST_ALL)
-    assert m.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d2")
+    # 128 brick-rows: three stages in flight per wave; 512 brick-rows: one
+    assert m.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d3")
+    tall = uw.Matrix(synth.weights(8192, 128, 1, 0.0005, 10), HOST_ALL)
+    assert tall.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d1")
     assert m.variant_in_use(1, uw.P1_FULL_DECODE)[1] == "hipblaslt"
     # the exponent form has no palette codes: the small kernel runs instead
     p, name = m.variant_in_use(1, uw.P2_EXP_DECODE)
@@ -168,3 +171,20 @@ def test_bits_per_weight_on_gate_shaped_slice():
     w = synth.weights(1024, 4096, 0, 0.0005, 10)
     inf = uw.Matrix(w, HOST_ALL).info()
     assert inf["bpw_palette"] < 16 * 0.8 and inf["bpw_huffman"] < 16 * 0.8
+
+
+def test_max_row_raw_matches_exported_tables():
+    """uw_info.max_row_raw (which selects the gemv kernel's LDS copy of the raw
+    groups) equals the largest per-brick-row raw count of the exported
+    tables; a matrix with no palette tables reports all ones."""
+    for rows, cols, p in ((256, 512, 0.003), (272, 1024, 0.02), (64, 4096, 0.0)):
+        w = synth.weights(rows, cols, 5, p, 12)
+        m = uw.Matrix(w, HOST_ALL)
+        rawmap = m.export(uw.STREAM_RAWMAP)
+        before = m.export(uw.STREAM_RAWBEFORE)
+        kbn = cols // 64
+        counts = [int(before[b + kbn - 1]) + bin(int(rawmap[b + kbn - 1])).count("1") - int(before[b])
+                  for b in range(0, len(rawmap), kbn)]
+        assert m.info()["max_row_raw"] == max(counts)
+    h = uw.Matrix(synth.weights(256, 512, 5, 0.003, 12), uw.FMT_HUFFMAN | uw.ENC_HOST_ONLY)
+    assert h.info()["max_row_raw"] == 0xFFFFFFFF
