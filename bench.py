@@ -159,7 +159,7 @@ def sweep(torch, uw, synth, stream, steps, warmup):
             y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
             row = {}
             flops = 2.0 * tokens * rows * cols
-            for p in (1, 2, 3, 4):
+            for p in (1, 2, 3, 4, 5):
                 i = [0]
 
                 def fn(p=p):

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libuw.so")
 # enums and flags of uw.h
 OK = 0
 ERR_INVALID_ARG, ERR_SHAPE, ERR_OOM, ERR_HIP, ERR_FORMAT, ERR_UNSUPPORTED, ERR_NO_DEVICE, ERR_IO = 1, 2, 3, 4, 5, 6, 7, 8
-P_AUTO, P1_FULL_DECODE, P2_EXP_DECODE, P3_PALETTE_TRANSCODE, P4_DIRECT_PALETTE = 0, 1, 2, 3, 4
+P_AUTO, P1_FULL_DECODE, P2_EXP_DECODE, P3_PALETTE_TRANSCODE, P4_DIRECT_PALETTE, P5_PALETTE_DECODE = 0, 1, 2, 3, 4, 5
 FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 (STREAM_SM, STREAM_NIBBLES, STREAM_RAWMAP, STREAM_RAWBEFORE, STREAM_SIDE, STREAM_WORDS, STREAM_OFFSETS,
  STREAM_PALETTE, STREAM_LENGTHS) = range(9)
@@ -45,7 +45,7 @@ class Info(C.Structure):
         ("code_lengths", C.c_uint8 * 256), ("raw_groups", C.c_uint64), ("groups", C.c_uint64),
         ("stream_bits", C.c_uint64), ("stream_words", C.c_uint64), ("bpw_palette", C.c_double),
         ("bpw_huffman", C.c_double), ("bpw_resident", C.c_double), ("resident_bytes", C.c_uint64),
-        ("scratch_bytes", C.c_uint64 * 5), ("max_row_raw", C.c_uint32),
+        ("scratch_bytes", C.c_uint64 * 6), ("max_row_raw", C.c_uint32),
     ]
 
 

@@ -166,7 +166,8 @@ struct uw_matrix {
     // chunks (512 x 256 weights)
     const size_t n = size_t(rows) * size_t(cols), groups = (n / 256 + 511) / 512;
     switch (p) {
-      case 1: return align256(2 * n);
+      case 1:
+      case 5: return align256(2 * n);
       case 2: return groups * 512 * 256;
       case 3: return groups * 512 * 128;
       default: return 0;
@@ -220,7 +221,8 @@ uw_status check_pipeline(const uw_matrix* h, int p) {
         return fail(UW_ERR_UNSUPPORTED, "pipeline 3 needs the Huffman format and the palette tables");
       return UW_OK;
     case 4:
-      if (!h->has(UW_FMT_PALETTE)) return fail(UW_ERR_UNSUPPORTED, "pipeline 4 needs the palette format");
+    case 5:
+      if (!h->has(UW_FMT_PALETTE)) return fail(UW_ERR_UNSUPPORTED, "pipeline %d needs the palette format", p);
       return UW_OK;
     default:
       return fail(UW_ERR_INVALID_ARG, "unknown pipeline %d", p);
@@ -265,6 +267,10 @@ uw_status ensure_scratch(uw_matrix* h, int p) {
 }
 
 uw_status launch_preprocess(uw_matrix* h, int p, hipStream_t s) {
+  if (p == 5) {
+    UW_HIP(uw::launch_palette_decode(fused_view(h, false, h->d_nib), (uint16_t*)h->scratch, s));
+    return UW_OK;
+  }
   const uw::HuffDev d = huff_view(h);
   const uw::DecodeEmit emit = p == 1 ? uw::EMIT_BF16 : p == 2 ? uw::EMIT_EXP : uw::EMIT_NIBBLE;
   UW_HIP(uw::launch_huff_decode(d, emit, h->scratch, s));
@@ -314,8 +320,9 @@ uw_status matmul_impl(uw_matrix* h, const uint16_t* x, float* y, int64_t tokens,
       UW_HIP(uw::launch_fused(fused_view(h, p == 2, (const uint8_t*)h->scratch), x, y, tokens, v, h->main));
       return mark_consumed(h);
     }
-    case 1: {
-      if ((st = prepare(h, 1)) != UW_OK) return st;
+    case 1:
+    case 5: {
+      if ((st = prepare(h, p)) != UW_OK) return st;
       if ((st = gemm_bf16(x, (const uint16_t*)h->scratch, y, tokens, h->rows, h->cols, h->main)) != UW_OK) return st;
       return mark_consumed(h);
     }
@@ -695,7 +702,8 @@ uw_status uw_matmul(uw_handle h, const uint16_t* x_dev, float* y_dev, int64_t to
 uw_status uw_preprocess(uw_handle h, int pipeline) {
   if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
   if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
-  if (pipeline < 1 || pipeline > 3) return fail(UW_ERR_UNSUPPORTED, "pipeline %d has no preprocessing", pipeline);
+  if (pipeline < 1 || pipeline == 4 || pipeline > 5)
+    return fail(UW_ERR_UNSUPPORTED, "pipeline %d has no preprocessing", pipeline);
   uw_status st = check_pipeline(h, pipeline);
   if (st != UW_OK) return st;
   if ((st = ensure_scratch(h, pipeline)) != UW_OK) return st;
@@ -737,7 +745,7 @@ uw_status uw_set_plan(uw_handle h, const int32_t* max_tokens, const int32_t* pip
   if (n < 0 || n > 16) return fail(UW_ERR_INVALID_ARG, "plan size %d out of range", n);
   if (n && (!max_tokens || !pipeline || !variant)) return fail(UW_ERR_INVALID_ARG, "null plan arrays");
   for (int i = 0; i < n; ++i) {
-    if (pipeline[i] < 1 || pipeline[i] > 4) return fail(UW_ERR_INVALID_ARG, "plan pipeline %d", pipeline[i]);
+    if (pipeline[i] < 1 || pipeline[i] > 5) return fail(UW_ERR_INVALID_ARG, "plan pipeline %d", pipeline[i]);
     uw_status st = check_pipeline(h, pipeline[i]);
     if (st != UW_OK) return st;
     if (variant[i] < 0 || variant[i] >= uw::variant_count(max_tokens[i]))
@@ -774,7 +782,7 @@ uw_status uw_variant_in_use(uw_handle h, int64_t tokens, int32_t pipeline, int32
     return fail(UW_ERR_INVALID_ARG, "variant %d does not exist for %lld tokens", var, (long long)tokens);
   if (pipeline_out) *pipeline_out = p;
   if (name && name_len) {
-    if (p == 1)
+    if (p == 1 || p == 5)
       snprintf(name, name_len, "hipblaslt");
     else
       uw::variant_describe(tokens, uw::variant_effective(tokens, h->rows, h->cols, p == 2, v), name, name_len);
@@ -810,7 +818,7 @@ uw_status uw_query(uw_handle h, uw_info* o) {
     bits += 32.0 * double(o->stream_words) + 32.0 * double((f.n() + uw::kChunk - 1) / uw::kChunk) + 2048.0;
   o->bpw_resident = bits / n;
   o->resident_bytes = h->dmem_bytes;
-  for (int p = 1; p <= 4; ++p) o->scratch_bytes[p] = h->scratch_need(p);
+  for (int p = 1; p <= 5; ++p) o->scratch_bytes[p] = h->scratch_need(p);
   return UW_OK;
 }
 
@@ -1161,7 +1169,7 @@ uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, i
   auto hard = [&](int l, int j, int* p) {
     int var = 0;
     *p = resolve_pipeline(handles[3 * l + j], tokens, pipelines[3 * l + j], &var);
-    return *p >= 1 && *p <= 3;
+    return *p != 4;  // pipelines 1-3 and 5 preprocess
   };
   auto issue_prep = [&](int l) -> uw_status {
     for (int j = 0; j < 3; ++j) {

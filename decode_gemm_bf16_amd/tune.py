@@ -91,7 +91,7 @@ def candidates(mat: Matrix) -> list[int]:
         if mat.formats & (FMT_PALETTE | 0x4):
             p.append(3)
     if mat.formats & FMT_PALETTE:
-        p.append(4)
+        p += [4, 5]
     return p
 
 

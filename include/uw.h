@@ -61,7 +61,9 @@ typedef enum {
                                or is not a bundle                             */
 } uw_status;
 
-/* Section 六: the four pipelines.  UW_P_AUTO picks from the plan set with
+/* Section 六: the four pipelines, and a fifth that is pipeline 1 fed from the
+ * direct-palette form (its full decode reads 1.5 bytes per weight instead of
+ * running the Huffman decoder).  UW_P_AUTO picks from the plan set with
  * uw_set_plan (else a built-in rule: direct palette when the handle has it,
  * else runtime palette transcode, else full decode). */
 typedef enum {
@@ -69,7 +71,8 @@ typedef enum {
   UW_P1_FULL_DECODE = 1,       /* Huffman -> bf16 W in scratch, then hipBLASLt     */
   UW_P2_EXP_DECODE = 2,        /* Huffman -> exponent bytes in scratch, fused GEMM */
   UW_P3_PALETTE_TRANSCODE = 3, /* Huffman -> 4-bit codes in scratch, fused GEMM    */
-  UW_P4_DIRECT_PALETTE = 4     /* resident 4-bit codes, fused GEMM, no preprocess  */
+  UW_P4_DIRECT_PALETTE = 4,    /* resident 4-bit codes, fused GEMM, no preprocess  */
+  UW_P5_PALETTE_DECODE = 5     /* palette form -> bf16 W in scratch, then hipBLASLt */
 } uw_pipeline;
 
 /* Format flags for uw_encode (section 四, section 六). */
@@ -112,7 +115,7 @@ typedef struct {
   double bpw_huffman;          /* bits/weight of the Huffman form               */
   double bpw_resident;         /* bits/weight of what this handle stores        */
   uint64_t resident_bytes;     /* compressed bytes held on the device           */
-  uint64_t scratch_bytes[5];   /* scratch that pipeline p (1..4) needs          */
+  uint64_t scratch_bytes[6];   /* scratch that pipeline p (1..5) needs          */
   uint32_t max_row_raw;        /* most raw groups in one brick-row of 16 rows   */
                                /* (0xFFFFFFFF: no palette tables)               */
 } uw_info;
@@ -133,17 +136,17 @@ uw_status uw_decode(uw_handle h, uint16_t* w_dev_out);
 
 /* Y[tokens, rows] = X[tokens, cols] * W^T through `pipeline` (section 六, 七).
  * x_dev, y_dev: device buffers as in the conventions.  tokens >= 1.
- * Pipelines 1-3 need UW_FMT_HUFFMAN (3 also PALETTE or RAWAUX), 4 needs
- * UW_FMT_PALETTE, else UW_ERR_UNSUPPORTED.  Pipelines 1-3 first run their
- * preprocessing into the handle's scratch unless uw_preprocess already queued
- * it, in which case the main stream waits for that work. */
+ * Pipelines 1-3 need UW_FMT_HUFFMAN (3 also PALETTE or RAWAUX), 4 and 5 need
+ * UW_FMT_PALETTE, else UW_ERR_UNSUPPORTED.  Pipelines 1-3 and 5 first run
+ * their preprocessing into the handle's scratch unless uw_preprocess already
+ * queued it, in which case the main stream waits for that work. */
 uw_status uw_matmul(uw_handle h, const uint16_t* x_dev, float* y_dev, int64_t tokens, int pipeline);
 
-/* Section 八: enqueue the preprocessing of `pipeline` (1-3) on the handle's
+/* Section 八: enqueue the preprocessing of `pipeline` (1-3, 5) on the handle's
  * side stream, writing the handle's scratch, and record an event that the next
  * uw_matmul with the same pipeline waits on.  Returns UW_ERR_UNSUPPORTED for
  * pipeline 4 or a missing format.
- * Scratch contents: pipeline 1, W as row-major bf16; pipelines 2 and 3, the
+ * Scratch contents: pipelines 1 and 5, W as row-major bf16; pipelines 2 and 3, the
  * exponent bytes (16 per run) or 4-bit codes (8 bytes per run) of the serial
  * order regrouped: with chunk c = 256 serial weights (16 runs of 16) and run r
  * of it, the run sits at run slot (c/512 * 16 + r) * 512 + c%512 (whole groups
@@ -154,7 +157,7 @@ uw_status uw_preprocess(uw_handle h, int pipeline);
  * stream defaults to the main stream. */
 uw_status uw_set_streams(uw_handle h, void* main_stream, void* side_stream);
 
-/* Caller-owned device scratch for pipelines 1-3 (at least
+/* Caller-owned device scratch for pipelines 1-3 and 5 (at least
  * uw_info.scratch_bytes[p] bytes, 256-byte aligned).  Without it the handle
  * allocates its own on first use.  Several handles may share one buffer when
  * their use does not overlap in time. */
@@ -279,8 +282,8 @@ size_t uw_mlp_workspace_bytes(int64_t tokens, int64_t inter);
 /* A stack of MLP layers (section 八): layer l uses handles[3l .. 3l+2]
  * (gate, up, down) and pipelines[3l .. 3l+2].  Each layer's input is the
  * previous layer's output rounded to bf16; y_dev gets the last layer's output.
- * With overlap != 0, the preprocessing of every hard projection (pipeline
- * 1-3) is issued on its handle's side stream one layer ahead, while the
+ * With overlap != 0, the preprocessing of every hard projection (pipelines
+ * 1-3 and 5) is issued on its handle's side stream one layer ahead, while the
  * previous layer computes; handles of consecutive layers must then not share
  * scratch.  work_dev: uw_stack_workspace_bytes(tokens, hidden, inter) bytes. */
 uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, int32_t layers,

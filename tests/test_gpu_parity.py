@@ -53,7 +53,7 @@ def test_mfma_fragment_layout_one_hot(env):
     ref_bits = w
     for tokens in (1, 5, 16, 17, 64, 65, 130):
         x, ks = synth.one_hot_activations(tokens, 256, seed=tokens)
-        for p in (1, 2, 3, 4):
+        for p in (1, 2, 3, 4, 5):
             y = _run(env, m, x, p)
             want = synth.bf16_bits_to_f32(ref_bits[:, ks].T.copy())
             assert np.array_equal(y, want), (tokens, p)
@@ -99,13 +99,13 @@ def test_preprocess_streams_bit_exact(env, data):
     inf = m.info()
     e_serial = oracle.to_serial(oracle.split(w)[0])
     pe = oracle.palette_encode(w)
-    for p, want in ((2, e_serial), (3, pe["nibbles"]), (1, w)):
+    for p, want in ((2, e_serial), (3, pe["nibbles"]), (1, w), (5, w)):
         buf = torch.empty(inf["scratch_bytes"][p], dtype=torch.uint8, device="cuda")
         m.set_scratch(buf)
         m.preprocess(p)
         torch.cuda.synchronize()
         got = buf.cpu().numpy()
-        if p == 1:
+        if p in (1, 5):
             got = got[: w.size * 2].view(np.uint16).reshape(w.shape)
         else:
             got = _serial_from_interleaved(got, w.size, 16 if p == 2 else 8)
@@ -123,7 +123,7 @@ def test_matmul_random_all_pipelines(env, shape, tokens):
     x = synth.activations(tokens, cols, xseed=1)
     ref = oracle.matmul_fp64(x, w)
     m = _both(env, w)
-    for p in (1, 2, 3, 4):
+    for p in (1, 2, 3, 4, 5):
         y = _run(env, m, x, p)
         assert np.isfinite(y).all(), p
         assert oracle.rel_err(y, ref) <= TOL, (p, oracle.rel_err(y, ref))
@@ -271,10 +271,10 @@ def test_gate_full_size_batch1(env):
     rows = np.random.default_rng(0).choice(c["rows"], 512, replace=False)
     ref = oracle.matmul_fp64_rows(x, w, rows)
     ys = {}
-    for p in (1, 2, 3, 4):
+    for p in (1, 2, 3, 4, 5):
         ys[p] = _run(env, m, x, p)
         assert oracle.rel_err(ys[p][:, rows], ref) <= TOL, p
-    for p in (1, 2, 3):
+    for p in (1, 2, 3, 5):
         assert oracle.rel_err(ys[p], ys[4]) <= TOL, p
 
 
@@ -290,7 +290,7 @@ def test_mlp_8b_shapes_sampled(env, proj):
     for tokens in (1, 16, 64, 256, 1024):
         x = xs[:tokens]
         ref = oracle.matmul_fp64_rows(x, w, sample)
-        for p in (1, 2, 3, 4):
+        for p in (1, 2, 3, 4, 5):
             y = _run(env, m, x, p)
             assert oracle.rel_err(y[:, sample], ref) <= TOL, (tokens, p)
 
@@ -387,11 +387,20 @@ def test_device_error_paths(env):
         mh.matmul(x, y, pipeline=uw.P3_PALETTE_TRANSCODE)
     assert e.value.status == uw.ERR_UNSUPPORTED
     with pytest.raises(uw.UwError) as e:
+        mh.matmul(x, y, pipeline=uw.P5_PALETTE_DECODE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        mh.preprocess(uw.P5_PALETTE_DECODE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
         mh.matmul(x, y, tokens=0)
     assert e.value.status == uw.ERR_INVALID_ARG
     mp = uw.Matrix(w, uw.FMT_PALETTE)
     with pytest.raises(uw.UwError) as e:
         mp.preprocess(uw.P1_FULL_DECODE)
+    assert e.value.status == uw.ERR_UNSUPPORTED
+    with pytest.raises(uw.UwError) as e:
+        mp.preprocess(uw.P4_DIRECT_PALETTE)
     assert e.value.status == uw.ERR_UNSUPPORTED
     with pytest.raises(uw.UwError) as e:
         mh.set_scratch(torch.empty(16, dtype=torch.uint8, device="cuda"))

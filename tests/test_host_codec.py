@@ -141,6 +141,7 @@ def test_variant_in_use_resolution():
     tall = uw.Matrix(synth.weights(8192, 128, 1, 0.0005, 10), HOST_ALL)
     assert tall.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d1")
     assert m.variant_in_use(1, uw.P1_FULL_DECODE)[1] == "hipblaslt"
+    assert m.variant_in_use(1024, uw.P5_PALETTE_DECODE) == (uw.P5_PALETTE_DECODE, "hipblaslt")
     # the exponent form has no palette codes: the small kernel runs instead
     p, name = m.variant_in_use(1, uw.P2_EXP_DECODE)
     assert p == uw.P2_EXP_DECODE and name.startswith("small:")
