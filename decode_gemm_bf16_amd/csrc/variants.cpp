@@ -147,10 +147,10 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // activations in LDS when they fit and there are enough brick-rows to
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
-    // (one stage in flight per wave when the brick-rows alone fill the chip,
-    // three for fewer, longer brick-rows)
+    // (8 waves per brick-row; the ring deepens with the bricks each wave
+    // streams: one stage in flight up to 8 bricks, two up to 16, else three)
     if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128)
-      return brows >= 512 ? Variant{2, 8, 1, 1, 0} : Variant{2, 8, 1, 3, 0};
+      return Variant{2, 8, 1, kbn <= 64 ? 1 : kbn <= 128 ? 2 : 3, 0};
     // from 12 tokens (20 for matrices too short to fill the chip without a
     // K split): four brick-rows per workgroup over the whole of K, the
     // activations streamed through LDS in 8-brick slices

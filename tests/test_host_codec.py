@@ -136,10 +136,12 @@ def test_variant_in_use_resolution():
     built-in rule, the exponent-form fallback of the LDS-activation shapes,
     an explicit variant and a plan."""
     m = uw.Matrix(synth.weights(2048, 4096, 1, 0.0005, 10), HOST_ALL)
-    # 128 brick-rows: three stages in flight per wave; 512 brick-rows: one
-    assert m.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d3")
-    tall = uw.Matrix(synth.weights(8192, 128, 1, 0.0005, 10), HOST_ALL)
-    assert tall.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d1")
+    # the ring depth follows the bricks per wave: 8 -> 1 stage, 16 -> 2, 28 -> 3
+    assert m.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, "gemv:w8:d1")
+    for cols, name in ((8192, "gemv:w8:d2"), (14336, "gemv:w8:d3")):
+        wide = uw.Matrix(synth.weights(2048, cols, 1, 0.0005, 10), HOST_ALL)
+        assert wide.variant_in_use(1) == (uw.P4_DIRECT_PALETTE, name), cols
+        wide.free()
     assert m.variant_in_use(1, uw.P1_FULL_DECODE)[1] == "hipblaslt"
     assert m.variant_in_use(1024, uw.P5_PALETTE_DECODE) == (uw.P5_PALETTE_DECODE, "hipblaslt")
     # the exponent form has no palette codes: the small kernel runs instead
