@@ -320,7 +320,7 @@ def test_mlp_layer_and_stack(env):
     xd = uw.bf16_tensor(x)
     y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
     work = torch.empty(uw.mlp_workspace_bytes(tokens, inter), dtype=torch.uint8, device="cuda")
-    for pipes in ([4, 4, 4], [1, 2, 3], [3, 3, 2]):
+    for pipes in ([4, 4, 4], [1, 2, 3], [3, 3, 2], [5, 4, 5]):
         uw.mlp_forward(*mats, pipes, xd, y, tokens, work)
         torch.cuda.synchronize()
         assert oracle.rel_err(y.cpu().numpy(), ref) <= 2 * TOL, pipes
@@ -346,7 +346,7 @@ def test_mlp_layer_and_stack(env):
             m.set_scratch(scratch[l % 2][j])
             m.set_variant(1)  # K not split across workgroups: no atomics, runs are bit-reproducible
             stack.append(m)
-            pipes.append(3 if l % 2 == 0 else 4)
+            pipes.append((3, 4, 5, 4)[l % 4])  # hard layers: runtime transcode, palette full decode
     work = torch.empty(uw.stack_workspace_bytes(tokens, hidden, inter), dtype=torch.uint8, device="cuda")
     outs = []
     for overlap in (False, True, True):
