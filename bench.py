@@ -187,6 +187,71 @@ def sweep(torch, uw, synth, stream, steps, warmup):
     return out
 
 
+def bf16_stack_ms(torch, uw, synth, c, x, tokens: int) -> float:
+    """One pass of the uncompressed 70B-shaped stack through hipBLASLt (ms):
+    2 distinct bf16 layers cycled, each 1.4 GB, so no layer is served from
+    the caches."""
+    L = c["layers"]
+    hidden, inter = c["gate"][1], c["gate"][0]
+    wd = [[uw.bf16_tensor(synth.weights(sh[0], sh[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"]))
+           for j, sh in enumerate((c["gate"], c["up"], c["down"]))] for l in range(2)]
+    g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
+    u = torch.empty_like(g)
+    h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
+    yb = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+    st = torch.cuda.Stream()
+
+    def bf16_pass():
+        for l in range(L):
+            wl = wd[l % 2]
+            uw.gemm_bf16(x, wl[0], g, tokens, inter, hidden, st)
+            uw.gemm_bf16(x, wl[1], u, tokens, inter, hidden, st)
+            uw.silu_mul(g, u, h, st)
+            uw.gemm_bf16(h, wl[2], yb, tokens, hidden, inter, st)
+    ms = time_graph(torch, bf16_pass, 2, 1, st, use_graph=False)
+    del wd
+    torch.cuda.empty_cache()
+    return ms
+
+
+def stack_p5_bench(torch, uw, synth, tokens: int, steps: int) -> dict:
+    """The 70B-shaped stack at a large batch with every layer in the direct-
+    palette form run through pipeline 5: each projection's full decode goes
+    to the side stream one layer ahead (two scratch slots per projection,
+    alternating between layers) while the previous layer's GEMMs run."""
+    from decode_gemm_bf16_amd.tune import tune_split
+    c = synth.CONFIGS["stack_70b"]
+    L = c["layers"]
+    hidden = c["gate"][1]
+    distinct = [[uw.Matrix(synth.weights(sh[0], sh[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"]), uw.FMT_PALETTE)
+                 for j, sh in enumerate((c["gate"], c["up"], c["down"]))] for l in range(2)]
+    stack = []
+    for l in range(L):
+        for j in range(3):
+            src = distinct[l % 2][j]
+            stack.append(src if l < 2 else src.clone())
+    pipes = [uw.P5_PALETTE_DECODE] * (3 * L)
+    scratch = [[torch.empty(distinct[0][j].info()["scratch_bytes"][5], dtype=torch.uint8, device="cuda")
+                for j in range(3)] for _ in range(2)]
+    for l in range(L):
+        for j in range(3):
+            stack[3 * l + j].set_scratch(scratch[l % 2][j])
+    x = uw.bf16_tensor(synth.activations(tokens, hidden, xseed=1))
+    res = tune_split(torch, stack, pipes, x, tokens, [0, uw.device_cu_count()], steps=steps, log=log)
+    serial = [ms for ms, n in res if n == 0][0]
+    overlap = [ms for ms, n in res if n != 0][0]
+    for m in stack:
+        m.free()
+    del scratch
+    torch.cuda.empty_cache()
+    bms = bf16_stack_ms(torch, uw, synth, c, x, tokens)
+    out = {"tokens": tokens, "layers": L, "pipeline": "P5 on every projection",
+           "serial_us": round(serial * 1e3, 1), "overlap_us": round(overlap * 1e3, 1),
+           "bf16_hipblaslt_us": round(bms * 1e3, 1)}
+    log("stack_p5", json.dumps(out))
+    return out
+
+
 def stack_bench(torch, uw, synth, tokens_list, steps: int):
     """The 70B-shaped stack: 80 SwiGLU layers (gate/up 28672x8192, down
     8192x28672), even layers hard (Huffman, runtime palette transcode), odd
@@ -235,24 +300,7 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
         serial = [ms for ms, n in res if n == 0][0]
         # all layers read as direct palette would need palette copies of the hard layers; time instead the
         # uncompressed bf16 stack: 4 distinct bf16 layers cycled (each 1.4 GB, no cache reuse across layers)
-        wd = [[uw.bf16_tensor(synth.weights(sh[0], sh[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"]))
-               for j, sh in enumerate((c["gate"], c["up"], c["down"]))] for l in range(2)]
-        g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
-        u = torch.empty_like(g)
-        h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
-        yb = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
-        st = torch.cuda.Stream()
-
-        def bf16_pass():
-            for l in range(L):
-                wl = wd[l % 2]
-                uw.gemm_bf16(x, wl[0], g, tokens, inter, hidden, st)
-                uw.gemm_bf16(x, wl[1], u, tokens, inter, hidden, st)
-                uw.silu_mul(g, u, h, st)
-                uw.gemm_bf16(h, wl[2], yb, tokens, hidden, inter, st)
-        bms = time_graph(torch, bf16_pass, 2, 1, st, use_graph=False)
-        del wd
-        torch.cuda.empty_cache()
+        bms = bf16_stack_ms(torch, uw, synth, c, x, tokens)
         out[str(tokens)] = {"serial_us": round(serial * 1e3, 1), "overlap_best_us": round(best_ms * 1e3, 1),
                             "best_side_cus": best_split, "splits": {str(n): round(ms * 1e3, 1) for ms, n in res},
                             "bf16_hipblaslt_us": round(bms * 1e3, 1),
@@ -617,6 +665,7 @@ def main() -> int:
         mats = []
         torch.cuda.empty_cache()
         result["stack"] = stack_bench(torch, uw, synth, [1, 256], steps=2)
+        result["stack"]["p5_1024"] = stack_p5_bench(torch, uw, synth, 1024, steps=2)
     if not args.no_cpu:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, x_bits, args.cpu_seconds)
