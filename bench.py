@@ -133,7 +133,7 @@ def load_traffic():
 
 
 def sweep(torch, uw, synth, stream, steps, warmup):
-    """All four pipelines and the uncompressed hipBLASLt baseline on the
+    """All five pipelines and the uncompressed hipBLASLt baseline on the
     8B-shaped MLP projections at batch 1..1024 (the other configurations)."""
     import numpy as np
     c = synth.CONFIGS["mlp_8b"]

@@ -1,7 +1,7 @@
 // C ABI (include/uw.h): handles, device upload, the four pipelines (Unweight
-// page, section 六), side-stream preprocessing (section 八), plans from the
+// page, section 六) and the palette-form full decode, side-stream preprocessing (section 八), plans from the
 // autotuner (section 九), the SwiGLU layer and layer-stack runners, and the
-// hipBLASLt call used by pipeline 1 and by the uncompressed baseline.
+// hipBLASLt call used by pipelines 1 and 5 and by the uncompressed baseline.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 #include <hipblaslt/hipblaslt.h>
