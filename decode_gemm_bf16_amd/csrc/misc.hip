@@ -79,12 +79,15 @@ __global__ __launch_bounds__(256) void palette_decode_kernel(const uint8_t* __re
                                                              const uint8_t* __restrict__ side, uint32_t lut0,
                                                              uint32_t lut1, uint32_t lut2, uint32_t lut3,
                                                              uint16_t* __restrict__ out, int64_t bricks, int cols) {
-  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t b = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   if (b >= bricks) return;
   const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
   const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
-  const u32x4 s = *(const u32x4*)(sm + b * 1024 + lane * 16);
-  const u32x2 n = *(const u32x2*)(nib + b * 512 + lane * 8);
+  // the compressed streams are read once: non-temporal loads; the bf16 output
+  // is read next by the GEMM, so its stores keep the default policy
+  const uint64_t nw = (uint64_t)bricks * 1024;
+  const u32x4 s = ld16s(make_rsrc(sm, nw), lane * 16, (uint32_t)b * 1024);
+  const u32x2 n = ld8s(make_rsrc(nib, nw / 2), lane * 8, (uint32_t)b * 512);
   const uint2 m = meta[b];
   uint32_t p[8];
   rebuild_palette(s, n, lut, p);
