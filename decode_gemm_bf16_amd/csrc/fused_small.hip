@@ -235,33 +235,30 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
   const uint32_t xl_step = live ? 128u : 0u;
 
   const int nmine = (kbn - wave + WAVES - 1) / WAVES;  // bricks kb = wave + WAVES*i of this wave
-  auto fetch = [&](GStage& st, int i, bool table_in_lds) {
+  // a stage's weight loads, and (from the LDS copy) its table entry
+  auto fetch_loads = [&](GStage& st, int i) {
     i = min(i, nmine - 1);  // a stage past the end re-reads the last brick; compute skips it
-    const int kb = wave + WAVES * i;
-    const uint2 m = table_in_lds ? ms[kb] : meta[brick_row0 + kb];
-    st.map = __builtin_amdgcn_readfirstlane(m.x);
-    st.before = __builtin_amdgcn_readfirstlane(m.y);
-    const uint32_t b = brick_row0 + kb;
+    const uint32_t b = brick_row0 + wave + WAVES * i;
     st.s = ld16s(rs_sm, lane16, b * 1024);
     st.n = ld8s(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
   };
+  auto fetch_table = [&](GStage& st, int i) {
+    const uint2 m = ms[wave + WAVES * min(i, nmine - 1)];
+    st.map = __builtin_amdgcn_readfirstlane(m.x);
+    st.before = __builtin_amdgcn_readfirstlane(m.y);
+  };
   GStage st[D];
-  if (nmine > 0) {  // the first stages read the table from global memory (scalar loads)
+  if (nmine > 0) {  // the first stages' table entries are read once the table is in LDS
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch(st[j], j, false);
+    for (int j = 0; j < D; ++j) fetch_loads(st[j], j);
   }
-  // the brick-row's raw groups: raw0 .. raw0 + nraw - 1
-  const uint2 m_first = meta[brick_row0], m_last = meta[brick_row0 + kbn - 1];
-  const uint32_t raw0 = __builtin_amdgcn_readfirstlane(m_first.y);
-  const uint32_t nraw = __builtin_amdgcn_readfirstlane(m_last.y) +
-                        __builtin_popcount(__builtin_amdgcn_readfirstlane(m_last.x)) - raw0;
+  uint32_t raw0 = 0;  // the brick-row's raw groups: raw0 .. raw0 + nraw - 1
   {
     constexpr int NT = WAVES * 64;
     constexpr int NXV = (kGemvX / 8 + NT - 1) / NT, NMV = (kGemvKbn + NT - 1) / NT;
     constexpr int NSV = SIDE_LDS ? (kGemvSideCap * 4 + NT - 1) / NT : 0;
     const rsrc_t rs_meta = make_rsrc(meta + brick_row0, (uint64_t)kbn * 8);
     const int n16 = tokens * cols / 8;
-    const uint32_t n16s = SIDE_LDS ? nraw * 4 : 0u;  // 16-byte pieces of the raw-group bytes
     u32x4 xv[NXV], sv[NSV > 0 ? NSV : 1];
     u32x2 mv[NMV];
 #pragma unroll
@@ -274,6 +271,15 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
       const int i = threadIdx.x + k * NT;
       xv[k] = ld16(rs_x, i < n16 ? i * 16 : kOffRange, 0);
     }
+    // x and the table are in flight before the wait for the two table
+    // entries that place the raw-group range (kept from being scheduled
+    // ahead of those loads)
+    __builtin_amdgcn_sched_barrier(0);
+    const uint2 m_first = meta[brick_row0], m_last = meta[brick_row0 + kbn - 1];
+    raw0 = __builtin_amdgcn_readfirstlane(m_first.y);
+    const uint32_t nraw = __builtin_amdgcn_readfirstlane(m_last.y) +
+                          __builtin_popcount(__builtin_amdgcn_readfirstlane(m_last.x)) - raw0;
+    const uint32_t n16s = SIDE_LDS ? nraw * 4 : 0u;  // 16-byte pieces of the raw-group bytes
 #pragma unroll
     for (int k = 0; k < NSV; ++k) {
       const uint32_t i = threadIdx.x + k * NT;
@@ -296,6 +302,10 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     }
     if (threadIdx.x < 2) ((u32x4*)(gemv_lds + xbytes))[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
+  }
+  if (nmine > 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) fetch_table(st[j], j);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const GStage& st, int i) {
@@ -328,7 +338,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       if (i + j < nmine) compute(st[j], i + j);
-      fetch(st[j], i + j + D, true);
+      fetch_loads(st[j], i + j + D);
+      fetch_table(st[j], i + j + D);
     }
   }
 
