@@ -191,3 +191,18 @@ def test_max_row_raw_matches_exported_tables():
         assert m.info()["max_row_raw"] == max(counts)
     h = uw.Matrix(synth.weights(256, 512, 5, 0.003, 12), uw.FMT_HUFFMAN | uw.ENC_HOST_ONLY)
     assert h.info()["max_row_raw"] == 0xFFFFFFFF
+
+
+def test_scratch_sizes_per_pipeline():
+    """uw_info.scratch_bytes: full decodes (pipelines 1 and 5) hold W as bf16,
+    256-byte aligned; pipelines 2 and 3 hold 16 exponent bytes / 8 code bytes
+    per run, padded to whole groups of 512 chunks of 256 weights; pipeline 4
+    needs none."""
+    rows, cols = 272, 576
+    m = uw.Matrix(synth.weights(rows, cols, 2, 0.003, 12), HOST_ALL)
+    sb = m.info()["scratch_bytes"]
+    n = rows * cols
+    groups = (n // 256 + 511) // 512
+    assert sb[1] == sb[5] == (2 * n + 255) // 256 * 256
+    assert sb[2] == groups * 512 * 256 and sb[3] == groups * 512 * 128
+    assert sb[4] == 0
