@@ -20,6 +20,7 @@
 #include "../../include/uw.h"
 #include "codec.h"
 #include "kernels.h"
+#include "runtime_internal.h"
 #include "transcode.h"
 
 namespace {
@@ -76,17 +77,26 @@ struct GemmPlan {
 };
 std::mutex g_blas_mu;
 hipblasLtHandle_t g_blas = nullptr;
-void* g_blas_ws = nullptr;
 constexpr size_t kBlasWs = size_t(64) << 20;
 std::map<std::tuple<int64_t, int64_t, int64_t>, GemmPlan> g_plans;
+// One hipBLASLt workspace per stream: library GEMMs in flight on different
+// streams (split-K algorithms write the workspace) must not share one.
+std::map<hipStream_t, void*> g_blas_ws;
 
 uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, int64_t n, int64_t k,
                     hipStream_t s) {
   std::lock_guard<std::mutex> lk(g_blas_mu);
-  if (!g_blas) {
-    if (hipblasLtCreate(&g_blas) != HIPBLAS_STATUS_SUCCESS) return fail(UW_ERR_HIP, "hipblasLtCreate failed");
-    if (hipMalloc(&g_blas_ws, kBlasWs) != hipSuccess) return fail(UW_ERR_OOM, "hipBLASLt workspace");
+  if (!g_blas && hipblasLtCreate(&g_blas) != HIPBLAS_STATUS_SUCCESS) {
+    g_blas = nullptr;
+    return fail(UW_ERR_HIP, "hipblasLtCreate failed");
   }
+  void*& ws_of_stream = g_blas_ws[s];
+  if (!ws_of_stream && hipMalloc(&ws_of_stream, kBlasWs) != hipSuccess) {
+    ws_of_stream = nullptr;
+    g_blas_ws.erase(s);
+    return fail(UW_ERR_OOM, "hipBLASLt workspace");
+  }
+  void* const ws = ws_of_stream;
   auto key = std::make_tuple(m, n, k);
   auto it = g_plans.find(key);
   if (it == g_plans.end()) {
@@ -121,7 +131,7 @@ uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, i
   const float alpha = 1.f, beta = 0.f;
   GemmPlan& p = it->second;
   hipblasStatus_t hs = hipblasLtMatmul(g_blas, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.c, y, p.c, &p.algo,
-                                       g_blas_ws, kBlasWs, s);
+                                       ws, kBlasWs, s);
   if (hs != HIPBLAS_STATUS_SUCCESS) return fail(UW_ERR_HIP, "hipblasLtMatmul failed (%d)", (int)hs);
   return UW_OK;
 }
@@ -286,7 +296,12 @@ uw_status prepare(uw_matrix* h, int p) {
     h->prep_pipeline = 0;
     return UW_OK;
   }
-  h->prep_pipeline = 0;
+  if (h->prep_pipeline != 0) {
+    // the side stream is still writing this scratch for another pipeline:
+    // the main stream's own preprocessing must not start before it ends
+    UW_HIP(hipStreamWaitEvent(h->main, h->prep_done, 0));
+    h->prep_pipeline = 0;
+  }
   return launch_preprocess(h, p, h->main);
 }
 
@@ -297,9 +312,18 @@ uw_status mark_consumed(uw_matrix* h) {
   return UW_OK;
 }
 
-uw_status matmul_impl(uw_matrix* h, const uint16_t* x, float* y, int64_t tokens, int pipeline) {
+// The fused kernels address the activations through a buffer resource whose
+// range is a 32-bit byte count (recon.h, make_rsrc): X may hold at most this
+// many bytes on pipelines 2-4.  The library GEMM of pipelines 1 and 5 has no
+// such limit.
+constexpr int64_t kMaxFusedXBytes = 0x7FFFFFF0;
+
+// Everything uw_matmul checks before it launches: arguments, shape limits,
+// the pipeline and variant.  Host only, so that it also runs on host-only
+// handles (which then fail with UW_ERR_UNSUPPORTED after these checks).
+uw_status matmul_check(const uw_matrix* h, const void* x, const void* y, int64_t tokens, int pipeline, int* p_out,
+                       uw::Variant* v_out) {
   if (!h) return fail(UW_ERR_INVALID_ARG, "null handle");
-  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
   if (!x || !y) return fail(UW_ERR_INVALID_ARG, "null activation or output pointer");
   if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
   if (tokens > (int64_t(1) << 24)) return fail(UW_ERR_INVALID_ARG, "tokens too large");
@@ -307,9 +331,23 @@ uw_status matmul_impl(uw_matrix* h, const uint16_t* x, float* y, int64_t tokens,
   const int p = resolve_pipeline(h, tokens, pipeline, &var);
   uw_status st = check_pipeline(h, p);
   if (st != UW_OK) return st;
+  if ((p == 2 || p == 3 || p == 4) && tokens * h->cols * 2 > kMaxFusedXBytes)
+    return fail(UW_ERR_SHAPE, "pipeline %d: activations of %lld x %lld bf16 exceed the fused kernels' %lld-byte limit",
+                p, (long long)tokens, (long long)h->cols, (long long)kMaxFusedXBytes);
   uw::Variant v = uw::variant_default(tokens, h->rows, h->cols);
   if (var != 0 && !uw::variant_get(tokens, var, &v))
     return fail(UW_ERR_INVALID_ARG, "variant %d does not exist for %lld tokens", var, (long long)tokens);
+  if (h->host_only) return fail(UW_ERR_UNSUPPORTED, "host-only handle");
+  *p_out = p;
+  *v_out = v;
+  return UW_OK;
+}
+
+uw_status matmul_impl(uw_matrix* h, const uint16_t* x, float* y, int64_t tokens, int pipeline) {
+  int p = 0;
+  uw::Variant v;
+  uw_status st = matmul_check(h, x, y, tokens, pipeline, &p, &v);
+  if (st != UW_OK) return st;
   switch (p) {
     case 4:
       UW_HIP(uw::launch_fused(fused_view(h, false, h->d_nib), x, y, tokens, v, h->main));
@@ -630,6 +668,53 @@ uw_status load_impl(const char* path, uint32_t formats, uw_matrix* h) {
 }
 
 }  // namespace
+
+namespace uw {
+
+uw_status set_error(uw_status st, const char* msg) { return fail(st, "%s", msg); }
+
+// One SwiGLU layer: gate and up into the workspace, h = silu(g) * u, down.
+// Every projection is checked before anything is launched.  fused_only
+// restricts the projections to pipeline 4, whose kernels need no
+// preprocessing scratch and no library GEMM workspace, so the call allocates
+// nothing.
+uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, const int32_t* pipelines,
+                           const uint16_t* x_dev, float* y_dev, int64_t tokens, void* work_dev, size_t work_bytes,
+                           bool fused_only) {
+  if (!gate || !up || !down || !pipelines || !x_dev || !y_dev || !work_dev)
+    return fail(UW_ERR_INVALID_ARG, "null argument");
+  const int64_t inter = gate->rows, hidden = gate->cols;
+  if (up->rows != inter || up->cols != hidden || down->rows != hidden || down->cols != inter)
+    return fail(UW_ERR_SHAPE, "gate/up [inter, hidden] and down [hidden, inter] shapes disagree");
+  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
+  if (up->main != gate->main || down->main != gate->main)
+    return fail(UW_ERR_INVALID_ARG, "gate, up and down must share one main stream");
+  if (work_bytes < uw_mlp_workspace_bytes(tokens, inter))
+    return fail(UW_ERR_INVALID_ARG, "workspace of %zu bytes, %lld tokens need %zu", work_bytes, (long long)tokens,
+                uw_mlp_workspace_bytes(tokens, inter));
+  uw_matrix* const hs[3] = {gate, up, down};
+  for (int j = 0; j < 3; ++j) {
+    int p = 0;
+    Variant v;
+    // x_dev stands in for each projection's input: only non-null is checked
+    uw_status st = matmul_check(hs[j], x_dev, y_dev, tokens, pipelines[j], &p, &v);
+    if (st != UW_OK) return st;
+    if (fused_only && p != 4)
+      return fail(UW_ERR_UNSUPPORTED, "projection %d resolves to pipeline %d; only pipeline 4 runs without allocating",
+                  j, p);
+  }
+  uint8_t* cur = static_cast<uint8_t*>(work_dev);
+  float* g = carve<float>(cur, size_t(tokens) * inter * 4);
+  float* u = carve<float>(cur, size_t(tokens) * inter * 4);
+  uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
+  uw_status st;
+  if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
+  if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;
+  UW_HIP(launch_silu_mul(g, u, hh, tokens * inter, gate->main));
+  return matmul_impl(down, hh, y_dev, tokens, pipelines[2]);
+}
+
+}  // namespace uw
 
 extern "C" {
 
@@ -1088,6 +1173,14 @@ uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t*
   }
   for (int32_t e = 0; e < n; ++e)
     if (experts[e]->host_only) return fail(UW_ERR_UNSUPPORTED, "expert %d is not on the device", e);
+  for (int32_t e = 0; e < n; ++e) {
+    const int64_t t = row_offsets[e + 1] - row_offsets[e];
+    if (t == 0) continue;
+    int p = 0;
+    uw::Variant v;
+    uw_status st = matmul_check(experts[e], x_dev, y_dev, t, pipeline, &p, &v);
+    if (st != UW_OK) return st;
+  }
   const int64_t rows = experts[0]->rows, cols = experts[0]->cols;
   for (int32_t e = 0; e < n; ++e) {
     const int64_t t = row_offsets[e + 1] - row_offsets[e];
@@ -1130,22 +1223,7 @@ size_t uw_mlp_workspace_bytes(int64_t tokens, int64_t inter) {
 
 uw_status uw_mlp_forward(uw_handle gate, uw_handle up, uw_handle down, const int32_t* pipelines,
                          const uint16_t* x_dev, float* y_dev, int64_t tokens, void* work_dev, size_t work_bytes) {
-  if (!gate || !up || !down || !pipelines || !x_dev || !y_dev || !work_dev)
-    return fail(UW_ERR_INVALID_ARG, "null argument");
-  const int64_t inter = gate->rows, hidden = gate->cols;
-  if (up->rows != inter || up->cols != hidden || down->rows != hidden || down->cols != inter)
-    return fail(UW_ERR_SHAPE, "gate/up [inter, hidden] and down [hidden, inter] shapes disagree");
-  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
-  if (work_bytes < uw_mlp_workspace_bytes(tokens, inter)) return fail(UW_ERR_INVALID_ARG, "workspace too small");
-  uint8_t* cur = static_cast<uint8_t*>(work_dev);
-  float* g = carve<float>(cur, size_t(tokens) * inter * 4);
-  float* u = carve<float>(cur, size_t(tokens) * inter * 4);
-  uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
-  uw_status st;
-  if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
-  if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;
-  UW_HIP(uw::launch_silu_mul(g, u, hh, tokens * inter, gate->main));
-  return matmul_impl(down, hh, y_dev, tokens, pipelines[2]);
+  return uw::mlp_forward_impl(gate, up, down, pipelines, x_dev, y_dev, tokens, work_dev, work_bytes, false);
 }
 
 size_t uw_stack_workspace_bytes(int64_t tokens, int64_t hidden, int64_t inter) {
@@ -1158,7 +1236,21 @@ uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, i
                            size_t work_bytes) {
   if (!handles || !pipelines || !x_dev || !y_dev || !work_dev || layers < 1)
     return fail(UW_ERR_INVALID_ARG, "bad argument");
+  if (tokens < 1) return fail(UW_ERR_INVALID_ARG, "tokens must be >= 1");
+  for (int i = 0; i < 3 * layers; ++i)
+    if (!handles[i]) return fail(UW_ERR_INVALID_ARG, "null handle %d", i);
   const int64_t inter = handles[0]->rows, hidden = handles[0]->cols;
+  for (int l = 0; l < layers; ++l) {
+    const uw_matrix* g = handles[3 * l];
+    const uw_matrix* u = handles[3 * l + 1];
+    const uw_matrix* d = handles[3 * l + 2];
+    // the workspace and the bf16 hand-over between layers are sized from layer 0
+    if (g->rows != inter || g->cols != hidden || u->rows != inter || u->cols != hidden || d->rows != hidden ||
+        d->cols != inter)
+      return fail(UW_ERR_SHAPE, "layer %d differs from layer 0's shape", l);
+    if (g->main != handles[0]->main || u->main != handles[0]->main || d->main != handles[0]->main)
+      return fail(UW_ERR_INVALID_ARG, "all handles must share one main stream (layer %d differs)", l);
+  }
   if (work_bytes < uw_stack_workspace_bytes(tokens, hidden, inter))
     return fail(UW_ERR_INVALID_ARG, "workspace too small");
   const size_t mlp_ws = uw_mlp_workspace_bytes(tokens, inter);
@@ -1185,7 +1277,6 @@ uw_status uw_stack_forward(const uw_handle* handles, const int32_t* pipelines, i
   if (overlap && (st = issue_prep(0)) != UW_OK) return st;
   const uint16_t* xin = x_dev;
   for (int l = 0; l < layers; ++l) {
-    if (handles[3 * l]->main != main) return fail(UW_ERR_INVALID_ARG, "all handles must share one main stream");
     if (overlap && l + 1 < layers && (st = issue_prep(l + 1)) != UW_OK) return st;
     int32_t p3[3];
     for (int j = 0; j < 3; ++j) {

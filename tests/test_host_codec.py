@@ -206,3 +206,49 @@ def test_scratch_sizes_per_pipeline():
     assert sb[1] == sb[5] == (2 * n + 255) // 256 * 256
     assert sb[2] == groups * 512 * 256 and sb[3] == groups * 512 * 128
     assert sb[4] == 0
+
+
+def test_fused_activation_limit_checked_on_the_host():
+    """The fused kernels (pipelines 2-4) address X through a 32-bit buffer
+    range: tokens x cols x 2 bytes above 0x7FFFFFF0 is UW_ERR_SHAPE, checked
+    before the handle's residency (a host-only handle reaches the check; no
+    device memory is touched, the pointers are never dereferenced).  The
+    library GEMM of pipelines 1 and 5 has no such limit."""
+    m = uw.Matrix(synth.weights(16, 4096, 1, 0.0, 0), HOST_ALL)
+    big = 1 << 18  # 2^18 tokens x 4096 columns x 2 bytes = 2^31 bytes
+    for p in (2, 3, 4):
+        assert uw._lib.uw_matmul(m._h, 8, 8, big, p) == uw.ERR_SHAPE, p
+        assert "limit" in uw.last_error()
+    for p in (1, 5):
+        assert uw._lib.uw_matmul(m._h, 8, 8, big, p) == uw.ERR_UNSUPPORTED, p
+    # one token less: 2^31 - 8192 bytes pass the check, then the host-only refusal
+    assert uw._lib.uw_matmul(m._h, 8, 8, big - 1, 4) == uw.ERR_UNSUPPORTED
+    # the grouped form checks every expert before launching any
+    offs = (C.c_int64 * 3)(0, 1, 1 + big)
+    hs = (C.c_void_p * 2)(m.handle, m.handle)
+    assert uw._lib.uw_grouped_matmul(hs, 2, 8, offs, 8, 4) == uw.ERR_UNSUPPORTED  # host-only first
+
+
+def test_layer_runner_host_checks():
+    """uw_mlp_forward and uw_stack_forward validate shapes, streams and token
+    counts of every projection before launching anything (host-only handles:
+    the last check standing is the residency one)."""
+    mk = lambda seed: uw.Matrix(synth.weights(64, 64, seed, 0.0, 0), HOST_ALL)
+    g, u, d = mk(1), mk(2), mk(3)
+    p3 = (C.c_int32 * 3)(4, 4, 4)
+    ws = uw._lib.uw_mlp_workspace_bytes(2, 64)
+    assert uw._lib.uw_mlp_forward(g._h, u._h, d._h, p3, 8, 8, 2, 8, ws) == uw.ERR_UNSUPPORTED
+    assert uw._lib.uw_mlp_forward(g._h, u._h, d._h, p3, 8, 8, 0, 8, ws) == uw.ERR_INVALID_ARG
+    assert uw._lib.uw_mlp_forward(g._h, u._h, d._h, p3, 8, 8, 2, 8, ws - 1) == uw.ERR_INVALID_ARG
+    u.set_streams(main=0x1000)  # never used: the check fails first
+    assert uw._lib.uw_mlp_forward(g._h, u._h, d._h, p3, 8, 8, 2, 8, ws) == uw.ERR_INVALID_ARG
+    assert "stream" in uw.last_error()
+    u.set_streams()
+    wide = uw.Matrix(synth.weights(128, 64, 4, 0.0, 0), HOST_ALL)  # a layer of another shape
+    hs = (C.c_void_p * 6)(g.handle, u.handle, d.handle, wide.handle, u.handle, d.handle)
+    p6 = (C.c_int32 * 6)(4, 4, 4, 4, 4, 4)
+    sws = uw._lib.uw_stack_workspace_bytes(2, 64, 64)
+    assert uw._lib.uw_stack_forward(hs, p6, 2, 8, 8, 2, 0, 8, sws) == uw.ERR_SHAPE
+    assert uw._lib.uw_stack_forward(hs, p6, 2, 8, 8, 0, 0, 8, sws) == uw.ERR_INVALID_ARG
+    hs_ok = (C.c_void_p * 6)(g.handle, u.handle, d.handle, g.handle, u.handle, d.handle)
+    assert uw._lib.uw_stack_forward(hs_ok, p6, 2, 8, 8, 2, 0, 8, sws) == uw.ERR_UNSUPPORTED
