@@ -135,7 +135,10 @@ uw_status uw_encode(const uint16_t* w_host, int64_t rows, int64_t cols, uint32_t
 uw_status uw_decode(uw_handle h, uint16_t* w_dev_out);
 
 /* Y[tokens, rows] = X[tokens, cols] * W^T through `pipeline` (section 六, 七).
- * x_dev, y_dev: device buffers as in the conventions.  tokens >= 1.
+ * x_dev, y_dev: device buffers as in the conventions.  1 <= tokens <= 2^24;
+ * on pipelines 2-4 (the fused kernels) X may hold at most 0x7FFFFFF0 bytes
+ * (tokens * cols * 2), else UW_ERR_SHAPE -- checked before anything else
+ * about the device, so host-only handles report it too.
  * Pipelines 1-3 need UW_FMT_HUFFMAN (3 also PALETTE or RAWAUX), 4 and 5 need
  * UW_FMT_PALETTE, else UW_ERR_UNSUPPORTED.  Pipelines 1-3 and 5 first run
  * their preprocessing into the handle's scratch unless uw_preprocess already
