@@ -27,7 +27,7 @@ FMT_HUFFMAN, FMT_PALETTE, FMT_RAWAUX, ENC_HOST_ONLY = 0x1, 0x2, 0x4, 0x100
 EXPORTED = [
     "uw_encode", "uw_decode", "uw_matmul", "uw_preprocess", "uw_set_streams", "uw_set_scratch", "uw_set_plan",
     "uw_set_variant", "uw_variant_name", "uw_variant_in_use", "uw_query", "uw_export", "uw_clone", "uw_save", "uw_load", "uw_upload", "uw_evict", "uw_grouped_matmul", "uw_free", "uw_last_error", "uw_silu_mul",
-    "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_stack_forward", "uw_stack_workspace_bytes",
+    "uw_mlp_forward", "uw_mlp_workspace_bytes", "uw_mlp_forward_noalloc", "uw_stack_forward", "uw_stack_workspace_bytes",
     "uw_stream_create", "uw_stream_destroy", "uw_device_cu_count", "uw_gemm_bf16", "uw_device_copy", "uw_device_read",
 ]
 
@@ -94,6 +94,7 @@ def _load() -> C.CDLL:
         "uw_silu_mul": ([vp, vp, vp, i64, vp], st),
         "uw_mlp_forward": ([vp, vp, vp, C.POINTER(i32), vp, vp, i64, vp, C.c_size_t], st),
         "uw_mlp_workspace_bytes": ([i64, i64], C.c_size_t),
+        "uw_mlp_forward_noalloc": ([vp, vp, vp, C.POINTER(i32), vp, vp, i64], st),
         "uw_stack_forward": ([C.POINTER(vp), C.POINTER(i32), i32, vp, vp, i64, i32, vp, C.c_size_t], st),
         "uw_stack_workspace_bytes": ([i64, i64, i64], C.c_size_t),
         "uw_stream_create": ([i32, i32, C.POINTER(vp)], st),
@@ -294,6 +295,16 @@ def mlp_forward(gate: Matrix, up: Matrix, down: Matrix, pipelines, x, y, tokens:
     p = (C.c_int32 * 3)(*pipelines)
     _check(_lib.uw_mlp_forward(gate._h, up._h, down._h, p, _ptr(x), _ptr(y), tokens, _ptr(work),
                                work.numel() * work.element_size()))
+
+
+STATIC_WORKSPACE_BYTES = 32 << 20  # UW_STATIC_WORKSPACE_BYTES
+
+
+def mlp_forward_noalloc(gate: Matrix, up: Matrix, down: Matrix, pipelines, x, y, tokens: int) -> None:
+    """The SwiGLU layer with the library's fixed device workspace (no allocation;
+    every projection must run the direct palette)."""
+    p = (C.c_int32 * 3)(*pipelines)
+    _check(_lib.uw_mlp_forward_noalloc(gate._h, up._h, down._h, p, _ptr(x), _ptr(y), tokens))
 
 
 def stack_workspace_bytes(tokens: int, hidden: int, inter: int) -> int:

@@ -282,6 +282,21 @@ uw_status uw_mlp_forward(uw_handle gate, uw_handle up, uw_handle down, const int
                          size_t work_bytes);
 size_t uw_mlp_workspace_bytes(int64_t tokens, int64_t inter);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer of
+ * uw_mlp_forward with its workspace (gate/up outputs and h) in a fixed device
+ * array of UW_STATIC_WORKSPACE_BYTES that the library holds on every device it
+ * runs on until the process ends.  Makes no allocation: every projection must
+ * resolve to pipeline 4 (direct palette, no preprocessing scratch, no library
+ * GEMM workspace), else UW_ERR_UNSUPPORTED.  UW_ERR_SHAPE when
+ * uw_mlp_workspace_bytes(tokens, inter) exceeds the array; other errors as
+ * uw_mlp_forward.  All calls on one device share its array: calls that
+ * overlap in time on one device (other streams, other threads) race and must
+ * be ordered by the caller.  Runs on gate's main stream. */
+#define UW_STATIC_WORKSPACE_BYTES (32u << 20)
+uw_status uw_mlp_forward_noalloc(uw_handle gate, uw_handle up, uw_handle down, const int32_t* pipelines,
+                                 const uint16_t* x_dev, float* y_dev, int64_t tokens);
+
 /* A stack of MLP layers (section 八): layer l uses handles[3l .. 3l+2]
  * (gate, up, down) and pipelines[3l .. 3l+2].  Each layer's input is the
  * previous layer's output rounded to bf16; y_dev gets the last layer's output.
