@@ -51,7 +51,7 @@ def test_tune_mlp_plan_and_parity(env):
             uw.mlp_forward(layer["gate"][1], layer["up"][1], layer["down"][1], [0, 0, 0], uw.bf16_tensor(x), y,
                            tokens, work)
         torch.cuda.synchronize()
-        assert oracle.rel_err(y.cpu().numpy(), ref) <= 2e-3, tokens
+        assert oracle.rel_err(y.cpu().numpy(), ref) <= 1e-3, tokens
 
 
 def test_tune_split_stack(env):
@@ -71,13 +71,15 @@ def test_tune_split_stack(env):
     res = tune.tune_split(torch, stack, pipes, uw.bf16_tensor(x), tokens, [0, 32, 128], steps=2, log=lambda s: None)
     assert sorted(n for _, n in res) == [0, 32, 128]
     assert all(ms > 0 for ms, _ in res)
-    # after the search the handles are back on the null stream; results still match the oracle
+    # after the search the handles are back on the null stream; each layer of
+    # the stack still matches the fp64 layer fed the bf16 input the GPU fed it
+    work = torch.empty(uw.stack_workspace_bytes(tokens, hidden, inter), dtype=torch.uint8, device="cuda")
     xin = x
     for l in range(L):
-        _, _, _, yl = oracle.mlp_layer_fp64(xin, *ws[l])
-        xin = oracle.f64_to_bf16_rne(yl)
-    work = torch.empty(uw.stack_workspace_bytes(tokens, hidden, inter), dtype=torch.uint8, device="cuda")
-    y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
-    uw.stack_forward(stack, pipes, uw.bf16_tensor(x), y, tokens, work, overlap=True)
-    torch.cuda.synchronize()
-    assert oracle.rel_err(y.cpu().numpy(), yl) <= 5e-3
+        y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        uw.stack_forward(stack[:3 * (l + 1)], pipes[:3 * (l + 1)], uw.bf16_tensor(x), y, tokens, work, overlap=True)
+        torch.cuda.synchronize()
+        yl = y.cpu().numpy()
+        _, _, _, ref = oracle.mlp_layer_fp64(xin, *ws[l])
+        assert oracle.rel_err(yl, ref) <= 1e-3, (l, oracle.rel_err(yl, ref))
+        xin = oracle.f64_to_bf16_rne(yl.astype(np.float64))

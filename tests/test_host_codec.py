@@ -252,3 +252,19 @@ def test_layer_runner_host_checks():
     assert uw._lib.uw_stack_forward(hs, p6, 2, 8, 8, 0, 0, 8, sws) == uw.ERR_INVALID_ARG
     hs_ok = (C.c_void_p * 6)(g.handle, u.handle, d.handle, g.handle, u.handle, d.handle)
     assert uw._lib.uw_stack_forward(hs_ok, p6, 2, 8, 8, 2, 0, 8, sws) == uw.ERR_UNSUPPORTED
+
+
+def test_library_bits_per_weight_count_its_exported_streams():
+    """uw_info's bits/weight of each form equal 8 x the bytes of the streams
+    uw_export hands out for that form (the 8-byte per-brick table counted as
+    the two exported 4-byte tables), divided by the weights."""
+    for w in (synth.weights(256, 512, 0, 0.001, 12), synth.weights(512, 4096, 0, 0.0005, 10)):
+        m = uw.Matrix(w, HOST_ALL)
+        info = m.info()
+        size = lambda s: m.export(s).nbytes
+        pal = sum(size(s) for s in (uw.STREAM_SM, uw.STREAM_NIBBLES, uw.STREAM_SIDE, uw.STREAM_RAWMAP,
+                                    uw.STREAM_RAWBEFORE, uw.STREAM_PALETTE))
+        huf = sum(size(s) for s in (uw.STREAM_SM, uw.STREAM_WORDS, uw.STREAM_OFFSETS, uw.STREAM_LENGTHS))
+        assert abs(info["bpw_palette"] - 8 * pal / w.size) < 1e-12
+        assert abs(info["bpw_huffman"] - 8 * huf / w.size) < 1e-12
+        m.free()

@@ -169,9 +169,47 @@ def test_pages_exponent_statistics_on_synthetic_weights():
     assert 2.3 < oracle.entropy_bits(cnt) < 2.9
 
 
-def test_palette_bits_per_weight_formula():
-    w = synth.weights(256, 512, 0, 0.001, 12)
+def _bpw_cases():
+    return {
+        "tiny": synth.weights(256, 512, 0, 0.001, 12),
+        "patterns": synth.all_bf16_patterns(),            # every group raw
+        "two_exponents": ((np.arange(64 * 128).reshape(64, 128) % 2) * 0x0080 + 0x3F00).astype(np.uint16),
+        "gate_slice": synth.weights(512, 4096, 0, 0.0005, 10),
+    }
+
+
+@pytest.mark.parametrize("name", ["tiny", "patterns", "two_exponents", "gate_slice"])
+def test_bits_per_weight_count_the_stored_arrays(name):
+    """bits/weight of each form = 8 x the bytes of the arrays its encoder
+    returns as the stored form, divided by the weights.  Palette form:
+    sign+mantissa bytes, 4-bit codes, raw side table, the two per-brick tables
+    and the palette.  Huffman form: sign+mantissa bytes, stream words, chunk
+    offsets and the code lengths.  The byte counts come from the arrays
+    themselves, so a dropped or miscounted term in either formula fails; the
+    side table must also hold 64 bytes for every raw group found by a direct
+    scan (section 四: a 64-weight row with an exponent outside the palette is
+    stored raw)."""
+    w = _bpw_cases()[name]
     enc = oracle.palette_encode(w)
-    n = 256 * 512
-    want = (12 * n + 512 * 92 + 64 * (16 * 8) + 128) / n
-    assert abs(oracle.palette_bits_per_weight(enc) - want) < 1e-12
+    stored = ("sm", "nibbles", "side", "brick_rawmap", "brick_rawbefore", "palette")
+    bits = 8 * sum(np.asarray(enc[k]).nbytes for k in stored)
+    assert abs(oracle.palette_bits_per_weight(enc) - bits / w.size) < 1e-12
+    e = (w.astype(np.uint32) >> 7) & 0xFF
+    in_pal = np.isin(e, np.asarray(enc["palette"]))
+    raw_scan = int((~in_pal.reshape(w.shape[0], -1, 64)).any(axis=2).sum())
+    assert enc["side"].nbytes == 64 * raw_scan
+    he = oracle.huffman_encode(w)
+    bits = 8 * sum(np.asarray(he[k]).nbytes for k in ("sm", "words", "offsets", "lengths"))
+    assert abs(oracle.huffman_bits_per_weight(he) - bits / w.size) < 1e-12
+
+
+def test_palette_form_at_least_20_percent_smaller_on_gate_statistics():
+    """The size target (>= 20% fewer weight bytes than bf16), from the byte
+    counts of the stored arrays on gate-statistics weights; the Huffman form too."""
+    w = synth.weights(1024, 4096, 0, 0.0005, 10)
+    enc = oracle.palette_encode(w)
+    stored = ("sm", "nibbles", "side", "brick_rawmap", "brick_rawbefore", "palette")
+    nbytes = sum(np.asarray(enc[k]).nbytes for k in stored)
+    assert nbytes <= 0.8 * 2 * w.size
+    he = oracle.huffman_encode(w)
+    assert sum(np.asarray(he[k]).nbytes for k in ("sm", "words", "offsets", "lengths")) <= 0.8 * 2 * w.size
