@@ -19,6 +19,10 @@ must read and write (compressed streams + activations + outputs) per second,
 against the 8 TB/s HBM peak.  cpu_baseline = the CPU oracle (numpy) doing the
 same decode + matmul on a bounded sample of the rows.
 
+The line also carries the same gate at 16-1024 tokens ("batches": direct
+palette, palette full decode + library GEMM, uncompressed library GEMM) and
+the batch-1024 figure against the bf16 MFMA peak ("roofline_batch1024").
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
 """
 from __future__ import annotations
@@ -43,9 +47,12 @@ KERNEL_SOURCES = ["decode_gemm_bf16_amd/csrc/fused_small.hip", "decode_gemm_bf16
                   "decode_gemm_bf16_amd/csrc/variants.cpp", "decode_gemm_bf16_amd/csrc/kernels.h"]
 
 
+LEAD_IN = None  # set in main(): untimed device work enqueued before each timed region
+
+
 def time_graph(torch, fn, steps, warmup, stream, use_graph=True):
     from decode_gemm_bf16_amd.tune import time_graph as tg
-    return tg(torch, fn, steps, warmup, stream, use_graph)
+    return tg(torch, fn, steps, warmup, stream, use_graph, lead_in=LEAD_IN)
 
 
 def kernel_sha() -> str:
@@ -74,13 +81,26 @@ def kernel_label(name: str, tokens: int, max_row_raw: int = 0) -> str:
 
 
 def cpu_baseline(w, x, seconds: float) -> dict:
-    """The CPU oracle decoding the palette form and doing the fp64 matmul on
-    2048-row slices of the same matrix, repeated for about `seconds`."""
+    """The CPU oracle on bounded samples of the same workload: palette decode +
+    fp64 matmul on 2048-row slices of the matrix, repeated for about `seconds`
+    (the reported value, effective weight GB/s as on the GPU); plus the
+    oracle's encoder (both forms) on one slice and its per-symbol Huffman
+    decoder on 64 chunks, as rates."""
     import numpy as np
     import oracle
     rows_per = 2048
     n_slices = w.shape[0] // rows_per
+    t0 = time.perf_counter()
     encs = [oracle.palette_encode(w[i * rows_per:(i + 1) * rows_per]) for i in range(min(n_slices, 2))]
+    enc_pal_s = (time.perf_counter() - t0) / len(encs)
+    t0 = time.perf_counter()
+    henc = oracle.huffman_encode(w[:rows_per])
+    enc_huf_s = time.perf_counter() - t0
+    chunks = np.random.default_rng(0).choice(len(henc["offsets"]), 64, replace=False)
+    t0 = time.perf_counter()
+    oracle.huffman_decode_chunks(henc, chunks)
+    dec_s = time.perf_counter() - t0
+    slice_bytes = 2 * rows_per * w.shape[1]
     done_rows = 0
     t0 = time.perf_counter()
     passes = 0
@@ -110,7 +130,57 @@ def cpu_baseline(w, x, seconds: float) -> dict:
     return {"value": round(eff, 5), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{passes} passes of oracle palette_decode + fp64 matmul on {rows_per}-row slices of the "
                       f"same {w.shape[0]}x{w.shape[1]} matrix at batch {x.shape[0]} ({el:.1f} s; numpy decode "
-                      f"single-threaded, BLAS {threads} threads; host {os.cpu_count()} cpus, {cpu_model})"}
+                      f"single-threaded, fp64 matmul on {threads} BLAS threads); encode rates on one "
+                      f"{rows_per}x{w.shape[1]} slice, Huffman decode on 64 random 256-symbol chunks",
+            "host_cpus": os.cpu_count(), "blas_threads": int(threads), "cpu_model": cpu_model,
+            "encode_palette_MBps": round(slice_bytes / enc_pal_s / 1e6, 2),
+            "encode_huffman_MBps": round(slice_bytes / enc_huf_s / 1e6, 2),
+            "huffman_decode_symbols_per_s": round(64 * 256 / dec_s, 1)}
+
+
+def batch_leg(torch, uw, synth, mats, wds, rows, cols, stream, steps, warmup) -> dict:
+    """The same gate at 16-1024 tokens, the rest of the metric's batch range:
+    the direct palette through the fused kernels (P4), the palette form fully
+    decoded and then multiplied by the library GEMM (P5, from 256 tokens, where
+    the GEMM is compute-bound), and the uncompressed hipBLASLt GEMM; compressed
+    copies and bf16 copies rotated as at batch 1.  TFLOP/s = 2*tokens*rows*cols
+    per second, against the bf16 MFMA peak."""
+    from decode_gemm_bf16_amd.tune import share_scratch
+    for m in mats:
+        m.set_variant(0)
+    shared = share_scratch(torch, mats)  # noqa: F841 (P5's decoded weights; kept alive while timing)
+    xs = synth.activations(1024, cols, xseed=1)
+    ncopy, nwd = len(mats), len(wds)
+    out = {}
+    for tokens in (16, 64, 256, 1024):
+        x = uw.bf16_tensor(xs[:tokens])
+        y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
+        flops = 2.0 * tokens * rows * cols
+        row = {}
+
+        def entry(ms):
+            tf = flops / ms / 1e9
+            return {"us": round(ms * 1e3, 2), "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "eff_GBps": round(2.0 * rows * cols / ms / 1e6, 1)}
+        for label, p in (("P4", 4), ("P5", 5)):
+            if p == 5 and tokens < 256:
+                continue
+            i = [0]
+
+            def fn(p=p):
+                mats[i[0] % ncopy].matmul(x, y, tokens, p)
+                i[0] += 1
+            row[label] = entry(time_graph(torch, fn, max(20, steps // 10), warmup, stream))
+        j = [0]
+
+        def blas():
+            uw.gemm_bf16(x, wds[j[0] % nwd], y, tokens, rows, cols, stream)
+            j[0] += 1
+        row["bf16_hipblaslt"] = entry(time_graph(torch, blas, max(20, steps // 10), warmup, stream))
+        row["P4_kernel"] = mats[0].variant_in_use(tokens, uw.P4_DIRECT_PALETTE)[1]
+        out[str(tokens)] = row
+        log(f"gate {tokens} tokens: " + json.dumps(row))
+    return out
 
 
 def load_traffic():
@@ -509,6 +579,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-batches", action="store_true", help="skip the 16-1024 token leg")
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
@@ -552,6 +623,12 @@ def main() -> int:
         m.set_variant(args.variant)
     x = uw.bf16_tensor(x_bits)
     y = torch.empty((tokens, rows), device="cuda", dtype=torch.float32)
+    # untimed lead-in before every timed region: a 512 MiB read keeps the
+    # device busy while the host submits the timed graph
+    global LEAD_IN
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    LEAD_IN = lambda: uw.device_read(flush, flush_sink, flush.numel(), stream)
 
     # algorithmic bytes of one launch: the streams the direct-palette kernel must
     # read (sign+mantissa, codes, per-brick table, raw side table) + x + y
@@ -589,6 +666,8 @@ def main() -> int:
         uw.gemm_bf16(x, wds[j[0] % wd_copies], y, tokens, rows, cols, stream)
         j[0] += 1
     bms = time_graph(torch, base_step, max(100, args.steps // 5), 10, stream, use_graph=not args.no_graph)
+    batches = None if args.no_batches else batch_leg(torch, uw, synth, mats, wds, rows, cols, stream, args.steps,
+                                                     args.warmup)
     del wds
     torch.cuda.empty_cache()
 
@@ -634,6 +713,15 @@ def main() -> int:
             "roofline_effective_GBps": round(HBM_PEAK_GBPS * 16 / pinfo["bpw_palette"], 1),
         },
     }
+    if batches is not None:
+        result["batches"] = batches
+        b = batches["1024"]
+        best = min(("P4", "P5"), key=lambda k: b[k]["us"])
+        result["roofline_batch1024"] = {
+            "bound": "mfma", "achieved": b["P4"]["TFLOPs"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": b["P4"]["mfma_frac"], "kernel": b["P4_kernel"], "avg_launch_us": b["P4"]["us"],
+            "best_compressed_route": best, "best_compressed_frac": b[best]["mfma_frac"],
+            "uncompressed_hipblaslt_frac": b["bf16_hipblaslt"]["mfma_frac"]}
     if args.sweep:
         result["sweep"] = sweep(torch, uw, synth, stream, args.steps, args.warmup)
     if args.tune:

@@ -32,10 +32,15 @@ from . import (FMT_HUFFMAN, FMT_PALETTE, Matrix, mlp_forward, mlp_workspace_byte
 PROJECTIONS = ("gate", "up", "down")
 
 
-def time_graph(torch, fn, steps: int, warmup: int, stream, use_graph: bool = True) -> float:
+def time_graph(torch, fn, steps: int, warmup: int, stream, use_graph: bool = True, lead_in=None) -> float:
     """Average milliseconds per call of fn() on `stream`, from HIP events
     around `steps` calls replayed from a HIP graph (eager launches if capture
-    is not possible)."""
+    is not possible).  With lead_in, an untimed run of the same steps and
+    then lead_in() are enqueued just before the start event, without a host
+    wait: the device is busy (and at the workload's clocks) while the host
+    submits the timed graph, so neither the submission latency nor a clock
+    ramp lands inside the timed region (both matter when `steps` is small);
+    lead_in should evict the caches (a large read)."""
     with torch.cuda.stream(stream):
         for _ in range(warmup):
             fn()
@@ -57,6 +62,15 @@ def time_graph(torch, fn, steps: int, warmup: int, stream, use_graph: bool = Tru
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
+        if lead_in is not None:
+            # the same steps once more, untimed and without a host wait, so the
+            # timed steps start at the clocks the workload runs at
+            if graph is not None:
+                graph.replay()
+            else:
+                for _ in range(steps):
+                    fn()
+            lead_in()
         start.record(stream)
         if graph is not None:
             graph.replay()
