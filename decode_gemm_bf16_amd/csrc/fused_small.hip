@@ -183,19 +183,45 @@ __global__ __launch_bounds__(WAVES * 64) void fused_small_kernel(
 
 // Few tokens whose activations fit in LDS (tokens x cols <= kGemvX): the same
 // brick-row-per-workgroup split, arranged so that each wave keeps only weight
-// bytes in its load pipeline.  At the start the workgroup copies x, its
+// bytes in its load pipeline.  At the start the workgroup moves x, its
 // brick-row's per-brick table and the raw groups' side-table bytes of the
-// brick-row (one contiguous range: raw groups are numbered in brick order)
-// into LDS, all loads issued before the one wait, so a brick costs two buffer
-// loads: sign+mantissa and codes.  A matrix with a brick-row of more raw
-// groups than the LDS copy holds (kGemvSideCap; a quarter of the groups at
-// 4096 columns) runs the SIDE_LDS = false form, which reads raw groups' bytes
-// from global memory when it meets them instead.  Each
-// wave runs a ring of D stages; the B operand comes from LDS at compute time;
-// partial sums are reduced one output per thread.
+// brick-row (one contiguous range: raw groups are numbered in brick order,
+// placed by the first and last table entries, read with scalar loads issued
+// first) straight from memory into LDS (buffer loads to LDS: no registers, no
+// LDS stores), behind the first weight loads, and waits once.  A brick then
+// costs two buffer loads: sign+mantissa and codes.  A matrix with a brick-row
+// of more raw groups than the LDS copy holds (kGemvSideCap; a quarter of the
+// groups at 4096 columns) runs the SIDE_LDS = false form, which reads raw
+// groups' bytes from global memory when it meets them instead.
+//
+// Each wave runs a ring of D + 1 register stages: the loads of brick i + D
+// are issued before brick i is rebuilt and multiplied, so D bricks are in
+// flight while one is computed.  The main loop holds no branch around the
+// loads (a load past the wave's last brick takes an out-of-range offset that
+// the buffer unit drops without a memory access), so the compiler's waits
+// count exactly the D stages behind the one computed; the last D bricks are
+// computed after the loop.  Partial sums are reduced one output per thread.
 constexpr int kGemvX = (int)kGemvXElems;   // bf16 elements of x held in LDS
 constexpr int kGemvKbn = (int)kGemvKbnMax;  // brick columns whose table fits the LDS copy
 constexpr int kGemvSideCap = 256;           // raw groups per brick-row whose bytes fit the LDS copy
+
+// 16 bytes per lane from a buffer straight into LDS: the wave's 64 lanes fill
+// the 1 KB at `lds` (wave-uniform) in lane order (4 bytes: 256 B).
+__device__ __forceinline__ void lds_dma16_g(rsrc_t r, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4_g(rsrc_t r, uint8_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, (int)voff, 0, 0, 0);
+}
+
+// LDS layout of the gemv kernel (bytes): [0, 32) zeros, read as x by the lanes
+// of absent tokens; x at kGemvX0, padded to 1 KB; the per-brick table, padded
+// to 256 B; the raw-group bytes, padded to 1 KB (whole DMA blocks everywhere:
+// lanes past the end of a copy may write zeros into the padding).
+constexpr uint32_t kGemvX0 = 1024;
+__host__ __device__ inline uint32_t gemv_xpad(uint32_t xbytes) { return (xbytes + 1023) & ~1023u; }
+__host__ __device__ inline uint32_t gemv_mpad(uint32_t kbn) { return (kbn * 8 + 255) & ~255u; }
+__host__ __device__ inline uint32_t gemv_spad(uint32_t cap) { return (cap * 64 + 1023) & ~1023u; }
 
 struct GStage {
   u32x4 s;          // sign+mantissa bytes
@@ -209,7 +235,8 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    uint64_t codes_bytes, int codes_ilv) {
+    uint64_t codes_bytes, int codes_ilv, int side_cap) {
+  constexpr int R = D + 1;  // register stages
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
@@ -221,92 +248,69 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
   const rsrc_t rs_codes = make_rsrc(codes, codes_bytes);
   const rsrc_t rs_side = make_rsrc(side, side_bytes);
   const rsrc_t rs_x = make_rsrc(x, (uint64_t)tokens * cols * 2);
+  const rsrc_t rs_meta = make_rsrc(meta + brick_row0, (uint64_t)kbn * 8);
   const uint32_t lane16 = lane * 16;
   const uint32_t clane = code_lane_off(q, r, 8, codes_ilv);
   const bool live = r < tokens;
-  // LDS: x (tokens x cols bf16), a 32-byte zero tail read by lanes of absent
-  // tokens, the brick-row's per-brick table, then (16-byte aligned) the
-  // brick-row's raw-group bytes
-  extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
+  extern __shared__ __attribute__((aligned(1024))) uint8_t gemv_lds[];
   const uint32_t xbytes = (uint32_t)tokens * cols * 2;
-  uint2* ms = (uint2*)(gemv_lds + xbytes + 32);
-  const uint8_t* sl = gemv_lds + ((xbytes + 32 + (uint32_t)kbn * 8 + 15) & ~15u);
-  const uint32_t xl_lane = live ? ((uint32_t)r * cols + q * 16) * 2 : xbytes;
+  uint8_t* lx = gemv_lds + kGemvX0;
+  uint8_t* lm = lx + gemv_xpad(xbytes);
+  const uint2* ms = (const uint2*)lm;
+  uint8_t* sl = lm + gemv_mpad(kbn);
+  const uint32_t xl_lane = live ? kGemvX0 + ((uint32_t)r * cols + q * 16) * 2 : 0u;
   const uint32_t xl_step = live ? 128u : 0u;
-
   const int nmine = (kbn - wave + WAVES - 1) / WAVES;  // bricks kb = wave + WAVES*i of this wave
-  // a stage's weight loads, and (from the LDS copy) its table entry
+
+  // the first and last table entries place the brick-row's raw-group bytes
+  uint2 m_first = {0u, 0u}, m_last = {0u, 0u};
+  if (SIDE_LDS) {
+    m_first = meta[brick_row0];
+    m_last = meta[brick_row0 + kbn - 1];
+  }
+  // a stage's weight loads (past the wave's last brick: dropped by the range check)
   auto fetch_loads = [&](GStage& st, int i) {
-    i = min(i, nmine - 1);  // a stage past the end re-reads the last brick; compute skips it
+    const bool past = i >= nmine;
     const uint32_t b = brick_row0 + wave + WAVES * i;
-    st.s = ld16s(rs_sm, lane16, b * 1024);
-    st.n = ld8s(rs_codes, clane, code_brick_off(b, 8, codes_ilv));
+    st.s = ld16s(rs_sm, past ? kOffRange : lane16, past ? 0u : b * 1024);
+    st.n = ld8s(rs_codes, past ? kOffRange : clane, past ? 0u : code_brick_off(b, 8, codes_ilv));
   };
   auto fetch_table = [&](GStage& st, int i) {
     const uint2 m = ms[wave + WAVES * min(i, nmine - 1)];
     st.map = __builtin_amdgcn_readfirstlane(m.x);
     st.before = __builtin_amdgcn_readfirstlane(m.y);
   };
-  GStage st[D];
-  if (nmine > 0) {  // the first stages' table entries are read once the table is in LDS
+  GStage st[R];
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch_loads(st[j], j);
+  for (int j = 0; j < D; ++j) fetch_loads(st[j], j);
+  if (threadIdx.x < 2) ((u32x4*)gemv_lds)[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+  {
+    const int n16 = (int)(xbytes / 16);
+    for (int c = wave; c * 64 < n16; c += WAVES) {
+      const int i = c * 64 + lane;
+      lds_dma16_g(rs_x, lx + c * 1024, i < n16 ? i * 16 : kOffRange);
+    }
+    const int nm4 = kbn * 2;
+    for (int c = wave; c * 64 < nm4; c += WAVES) {
+      const int i = c * 64 + lane;
+      lds_dma4_g(rs_meta, lm + c * 256, i < nm4 ? i * 4 : kOffRange);
+    }
   }
   uint32_t raw0 = 0;  // the brick-row's raw groups: raw0 .. raw0 + nraw - 1
-  {
-    constexpr int NT = WAVES * 64;
-    constexpr int NXV = (kGemvX / 8 + NT - 1) / NT, NMV = (kGemvKbn + NT - 1) / NT;
-    constexpr int NSV = SIDE_LDS ? (kGemvSideCap * 4 + NT - 1) / NT : 0;
-    const rsrc_t rs_meta = make_rsrc(meta + brick_row0, (uint64_t)kbn * 8);
-    const int n16 = tokens * cols / 8;
-    u32x4 xv[NXV], sv[NSV > 0 ? NSV : 1];
-    u32x2 mv[NMV];
-#pragma unroll
-    for (int k = 0; k < NMV; ++k) {
-      const int i = threadIdx.x + k * NT;
-      mv[k] = ld8(rs_meta, i < kbn ? i * 8 : kOffRange, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < NXV; ++k) {
-      const int i = threadIdx.x + k * NT;
-      xv[k] = ld16(rs_x, i < n16 ? i * 16 : kOffRange, 0);
-    }
-    // x and the table are in flight before the wait for the two table
-    // entries that place the raw-group range (kept from being scheduled
-    // ahead of those loads)
-    __builtin_amdgcn_sched_barrier(0);
-    const uint2 m_first = meta[brick_row0], m_last = meta[brick_row0 + kbn - 1];
+  if (SIDE_LDS) {
     raw0 = __builtin_amdgcn_readfirstlane(m_first.y);
     const uint32_t nraw = __builtin_amdgcn_readfirstlane(m_last.y) +
                           __builtin_popcount(__builtin_amdgcn_readfirstlane(m_last.x)) - raw0;
-    const uint32_t n16s = SIDE_LDS ? nraw * 4 : 0u;  // 16-byte pieces of the raw-group bytes
-#pragma unroll
-    for (int k = 0; k < NSV; ++k) {
-      const uint32_t i = threadIdx.x + k * NT;
-      sv[k] = ld16(rs_side, i < n16s ? raw0 * 64 + i * 16 : kOffRange, 0);
+    const int ns16 = (int)min(nraw, (uint32_t)side_cap) * 4;
+    for (int c = wave; c * 64 < ns16; c += WAVES) {
+      const int i = c * 64 + lane;
+      lds_dma16_g(rs_side, sl + c * 1024, i < ns16 ? raw0 * 64 + i * 16 : kOffRange);
     }
-#pragma unroll
-    for (int k = 0; k < NMV; ++k) {
-      const int i = threadIdx.x + k * NT;
-      if (i < kbn) ms[i] = uint2{mv[k].x, mv[k].y};
-    }
-#pragma unroll
-    for (int k = 0; k < NXV; ++k) {
-      const int i = threadIdx.x + k * NT;
-      if (i < n16) ((u32x4*)gemv_lds)[i] = xv[k];
-    }
-#pragma unroll
-    for (int k = 0; k < NSV; ++k) {
-      const uint32_t i = threadIdx.x + k * NT;
-      if (i < n16s) ((u32x4*)sl)[i] = sv[k];
-    }
-    if (threadIdx.x < 2) ((u32x4*)(gemv_lds + xbytes))[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
   }
-  if (nmine > 0) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < D; ++j) fetch_table(st[j], j);
-  }
+  for (int j = 0; j < D; ++j) fetch_table(st[j], j);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const GStage& st, int i) {
     const int kb = wave + WAVES * i;
@@ -334,43 +338,49 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0), as_bf16x8(xb0), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1), as_bf16x8(xb1), acc, 0, 0, 0);
   };
-  for (int i = 0; i < nmine; i += D) {
+  // brick i sits in stage i % R; brick i + D is requested before brick i is computed
+  int i = 0;
+  for (; i + R <= nmine; i += R) {
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      if (i + j < nmine) compute(st[j], i + j);
-      fetch_loads(st[j], i + j + D);
-      fetch_table(st[j], i + j + D);
+    for (int j = 0; j < R; ++j) {
+      fetch_loads(st[(j + D) % R], i + j + D);
+      fetch_table(st[(j + D) % R], i + j + D);
+      compute(st[j], i + j);
     }
   }
+#pragma unroll
+  for (int j = 0; j < R - 1; ++j)
+    if (i + j < nmine) compute(st[j], i + j);
 
   // partial sums of all waves; each output summed by one thread, waves in order
   __shared__ float red[WAVES][256];
   *(f32x4*)&red[wave][lane * 4] = acc;
   __syncthreads();
-  for (int i = threadIdx.x; i < 256; i += WAVES * 64) {
-    const int l = i >> 2, j = i & 3;
+  for (int k = threadIdx.x; k < 256; k += WAVES * 64) {
+    const int l = k >> 2, j = k & 3;
     const int tok = l & 15;  // D layout: lane l holds rows 4*(l/16)+0..3 of column (token) l%16
     if (tok >= tokens) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) sum += red[w][i];
+    for (int w = 0; w < WAVES; ++w) sum += red[w][k];
     y[(size_t)tok * rows + (size_t)blockIdx.x * 16 + 4 * (l >> 4) + j] = sum;
   }
 }
 
 template <int WAVES, int D>
 hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, hipStream_t s) {
-  const size_t head = (size_t)tokens * w.cols * 2 + 32 + (size_t)(w.cols / 64) * 8;
   const bool side_lds = w.max_row_raw <= (uint32_t)kGemvSideCap;
-  const size_t lds = side_lds ? ((head + 15) & ~(size_t)15) + (size_t)kGemvSideCap * 64 : head;
+  const uint32_t cap = side_lds ? w.max_row_raw : 0u;
+  const size_t lds = kGemvX0 + gemv_xpad((uint32_t)(tokens * w.cols * 2)) + gemv_mpad((uint32_t)(w.cols / 64)) +
+                     (side_lds ? gemv_spad(cap) : 0u);
   if (side_lds)
     hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D, true>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s,
                        w.sm, w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
-                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
+                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv, (int)cap);
   else
     hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D, false>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s,
                        w.sm, w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
-                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv);
+                       (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv, 0);
   return hipGetLastError();
 }
 
