@@ -147,10 +147,11 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // activations in LDS when they fit and there are enough brick-rows to
     // fill the chip without splitting K (the launch falls back to the small
     // kernel for the exponent form)
-    // (8 waves per brick-row; the ring deepens with the bricks each wave
-    // streams: one stage in flight up to 8 bricks, two up to 16, else three)
+    // (8 waves per brick-row, two bricks in flight while one is computed:
+    // measured best or within 1% on 14336x4096, 4096x14336, 28672x8192 and
+    // 128256x4096 at one token)
     if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128)
-      return Variant{2, 8, 1, kbn <= 64 ? 1 : kbn <= 128 ? 2 : 3, 0};
+      return Variant{2, 8, 1, 2, 0};
     // from 12 tokens (20 for matrices too short to fill the chip without a
     // K split): four brick-rows per workgroup over the whole of K, the
     // activations streamed through LDS in 8-brick slices
@@ -160,6 +161,11 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     const int64_t groups = (brows + 3) / 4;
     const Variant rowk = groups > 256 && groups <= 512 ? Variant{4, 2, 2, 2, 4} : Variant{4, 4, 2, 2, 4};
     if (tokens >= 12 && (tokens >= 20 || groups >= 128) && rowk_fits(tokens, rows, cols, rowk)) return rowk;
+    // fewer tokens whose activations do not fit the gemv kernel's LDS copy
+    // (long K, e.g. 8192x28672): the whole-K kernel where it fills the chip
+    // (58.6 against 61.6 us for the small kernel at one token)
+    if (tokens < 12 && groups >= 128 && rowk_fits(tokens, rows, cols, Variant{4, 4, 2, 2, 4}))
+      return Variant{4, 4, 2, 2, 4};
     // from 16 tokens: K slices of the activations in LDS shared by 8
     // brick-rows (the small kernel reads them from L2 once per brick-row)
     if (tokens >= 16) return Variant{3, 8, 1, 2, 0};
