@@ -23,16 +23,22 @@
 // LDS), palette codes through a 64-bit register queue whose low dword is
 // stored, aligned, after every lookup.  A run (16 symbols) is emitted once
 // both chains of every lane of the wave hold one; a chain may run up to half
-// a run ahead.  The 512 chunks' bits are first copied into LDS with
-// coalesced 16-byte loads (a workgroup whose span does not fit, which needs
-// more than 2.8 bits per exponent on average -- 3.3 for pipeline 3 -- reads
-// its words from global memory).
+// a run ahead.  The table and the workgroup's bits are first moved into LDS
+// by buffer loads straight to LDS (a workgroup whose span does not fit, which
+// needs more than 2.8 bits per exponent on average -- 3.3 for pipeline 3 --
+// reads its words from global memory).  The grid gives every workgroup the
+// same number of chunks (at most 512), chosen so that the workgroups fill
+// whole rounds of two per CU: on the 14336 x 4096 gate 512 workgroups of 448
+// chunks instead of 448 of 512, which left a quarter of the CUs with one
+// workgroup and the rest with two.
 //
 // A chunk is a quarter brick: 16 runs of 16 symbols, run i = row i of the
 // brick, 16 consecutive columns.  Pipelines 2 and 3 write run r of chunk c at
 // slot ((c / 512) * 16 + r) * 512 + c % 512: the workgroup's 512 chunks store
 // one run as one contiguous block, and the blocks of successive runs follow
 // each other.  Pipeline 1 writes bf16 W row-major.
+#include <algorithm>
+
 #include "kernels.h"
 #include "recon.h"
 
@@ -270,18 +276,26 @@ __device__ __forceinline__ void decode_codes(Src src, uint32_t base, int64_t ca,
   }
 }
 
+// 16 bytes per lane from a buffer straight into LDS: a wave's 64 lanes fill
+// the 1 KB at `lds` (wave-uniform) in lane order.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)voff, 0, 0, 0);
+}
+
 template <int EMIT>
 __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
     const uint32_t* __restrict__ words, uint64_t total_bits, const uint32_t* __restrict__ offsets,
     const uint32_t* __restrict__ lut_g, const uint8_t* __restrict__ sm, const uint2* __restrict__ meta,
-    void* __restrict__ out, uint64_t out_bytes, int64_t nchunks, int cols) {
+    void* __restrict__ out, uint64_t out_bytes, int64_t nchunks, int cols, int cpw) {
   constexpr int kStage = stage_words<EMIT>();
   constexpr int kSlotBytes = EMIT == EMIT_NIBBLE ? kCodeSlot * 4 : kSymSlot;
-  __shared__ uint32_t lut[4096];
-  __shared__ uint32_t stage[kStage];
+  static_assert(kStage % 256 == 0, "the stage takes whole 1 KB copy blocks");
+  __shared__ __attribute__((aligned(1024))) uint32_t lut[4096];
+  __shared__ __attribute__((aligned(1024))) uint32_t stage_buf[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t slots[kChunksPerBlock * kSlotBytes];
-  const int64_t c0 = (int64_t)blockIdx.x * kChunksPerBlock;
-  const int64_t c_end = c0 + kChunksPerBlock < nchunks ? c0 + kChunksPerBlock : nchunks;
+  // this workgroup's chunks: c0 .. c_end - 1, at most 2 * kThreads
+  const int64_t c0 = (int64_t)blockIdx.x * cpw;
+  const int64_t c_end = c0 + cpw < nchunks ? c0 + cpw : nchunks;
   // words read: from the first chunk's start to 5 words past the last
   // chunk's end (a chain keeps taking lookups while its slot has room: at
   // most 8 of at most 12 bits past its end; the bit buffer reads 2 words
@@ -289,42 +303,29 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   const uint32_t w0 = offsets[c0] >> 5;
   const uint64_t end_bit = c_end < nchunks ? (uint64_t)offsets[c_end] : total_bits;
   const uint32_t w1 = (uint32_t)(end_bit >> 5) + 6;
-  const bool staged = w1 - w0 <= (uint32_t)kStage;
+  // The copy starts at the 16-byte aligned word a0 <= w0 and writes whole
+  // 1 KB blocks (lanes past the span write zeros): those must fit the stage.
+  const uint32_t a0 = w0 & ~3u;
+  const bool staged = ((w1 - a0 + 255) & ~255u) <= (uint32_t)kStage;
+  const uint32_t* stage = stage_buf + (w0 - a0);  // stage[i] = word w0 + i
   {
-    // The table and the 16-byte aligned span of words [w0 & ~3, w1) go to
-    // LDS: every load is issued before the first store.
-    constexpr int LV = 4096 * 4 / 16 / kThreads;
-    constexpr int SV = (kStage / 4 + 2 + kThreads - 1) / kThreads;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const rsrc_t rs_lut = make_rsrc(lut_g, 4096 * 4);
     const rsrc_t rs_words = make_rsrc(words, (((total_bits + 31) >> 5) + kStreamPad) * 4);
-    const uint32_t a0 = w0 & ~3u;
+    for (int c = wave; c < 16; c += kThreads / 64) dma16(rs_lut, (uint8_t*)lut + c * 1024, (c * 64 + lane) * 16);
     const uint32_t nvec = staged ? (w1 - a0 + 3) / 4 : 0u;
-    u32x4 lv[LV], sv[SV];
-#pragma unroll
-    for (int k = 0; k < LV; ++k) lv[k] = ld16(rs_lut, (threadIdx.x + k * kThreads) * 16, 0);
-#pragma unroll
-    for (int k = 0; k < SV; ++k) {
-      const uint32_t i = threadIdx.x + k * kThreads;
-      sv[k] = ld16s(rs_words, i < nvec ? (a0 + 4 * i) * 4 : kOffRange, 0);
+    for (uint32_t c = wave; c * 64 < nvec; c += kThreads / 64) {
+      const uint32_t i = c * 64 + lane;
+      dma16(rs_words, (uint8_t*)stage_buf + c * 1024, i < nvec ? (a0 + 4 * i) * 4 : kOffRange);
     }
-#pragma unroll
-    for (int k = 0; k < LV; ++k) ((u32x4*)lut)[threadIdx.x + k * kThreads] = lv[k];
-#pragma unroll
-    for (int k = 0; k < SV; ++k) {
-      const uint32_t i = threadIdx.x + k * kThreads;
-      if (i < nvec) {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int32_t d = (int32_t)(a0 + 4 * i + kk) - (int32_t)w0;
-          if (d >= 0 && d < kStage) stage[d] = sv[k][kk];
-        }
-      }
-    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
-  const int64_t ca = c0 + threadIdx.x, cb = ca + kThreads;
-  if (ca >= nchunks) return;
-  const bool has_b = cb < nchunks;
+  // chain a of lane t decodes chunk c0 + t, chain b chunk c0 + half + t
+  const int half = (int)((c_end - c0 + 1) / 2);
+  if ((int)threadIdx.x >= half) return;
+  const int64_t ca = c0 + threadIdx.x, cb = ca + half;
+  const bool has_b = cb < c_end;
   const uint8_t* lutb = (const uint8_t*)lut;
   if constexpr (EMIT == EMIT_NIBBLE) {
     uint32_t* slot_a = (uint32_t*)slots + threadIdx.x * kCodeSlot;
@@ -349,6 +350,19 @@ __global__ __launch_bounds__(kThreads) void huff_decode_kernel(
   }
 }
 
+// Compute units of the current device (256 on MI355X), read once per device.
+int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipStream_t s) {
@@ -361,10 +375,17 @@ hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipS
                                                    : (uint64_t)nchunks * 512;
   // buffer stores take 32-bit offsets within a 2 GB range
   if (emit != EMIT_BF16 && out_bytes > 0x7FFFFFF0ull) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)groups);
+  // Chunks per workgroup: the fewest (a multiple of 64, at most 512) that
+  // fill whole rounds of two workgroups per CU (their LDS allows two).
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t rounds = (nchunks + slots * kChunksPerBlock - 1) / (slots * kChunksPerBlock);
+  int64_t cpw = (nchunks + slots * rounds - 1) / (slots * rounds);
+  cpw = std::min<int64_t>(kChunksPerBlock, ((cpw + 63) / 64) * 64);
+  const dim3 grid((unsigned)((nchunks + cpw - 1) / cpw));
 #define UW_LAUNCH(E)                                                                                           \
   hipLaunchKernelGGL(huff_decode_kernel<E>, grid, dim3(kThreads), 0, s, h.words, h.total_bits, h.offsets,          \
-                     E == EMIT_NIBBLE ? h.lut_codes : h.lut, h.sm, h.meta, out, out_bytes, nchunks, (int)h.cols)
+                     E == EMIT_NIBBLE ? h.lut_codes : h.lut, h.sm, h.meta, out, out_bytes, nchunks, (int)h.cols,   \
+                     (int)cpw)
   switch (emit) {
     case EMIT_BF16: UW_LAUNCH(EMIT_BF16); break;
     case EMIT_EXP: UW_LAUNCH(EMIT_EXP); break;
