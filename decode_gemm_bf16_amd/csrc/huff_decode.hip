@@ -134,25 +134,27 @@ __device__ __forceinline__ u32x4 take_sym_run(uint8_t* slot, uint32_t& p) {
   return e;
 }
 
-// Palette codes: an entry holds up to five codes (bits 0-19), their count
-// (24-26) and the bits they take (27-31).  They join the queue; its low dword
-// is stored at dword k of the slot and k moves on once the dword holds 8.
+// Palette codes: an entry holds up to five codes (bits 0-19), four times
+// their count (22-26) and the bits they take (27-31).  The codes not yet
+// completing a dword wait in q (qs bits of it); a lookup shifts its codes by
+// qs as one 64-bit value, stores q with their low part at byte kb of the slot,
+// and when the dword is full moves on to the next one, keeping the high part.
 struct CodeQ {
-  uint64_t q;
-  uint32_t qn, k;
+  uint32_t q, qs, kb;
 };
 
-__device__ __forceinline__ void lookup_code(BitBuf& bb, CodeQ& cq, bool take, uint32_t* slot, const uint8_t* lut) {
+__device__ __forceinline__ void lookup_code(BitBuf& bb, CodeQ& cq, bool take, uint8_t* slot, const uint8_t* lut) {
   uint32_t ent = table_entry(bb, lut);
   ent = take ? ent : 0u;
   bb.r -= (int32_t)(ent >> 27);
-  cq.q |= (uint64_t)(ent & 0xFFFFFu) << (4 * cq.qn);
-  cq.qn += (ent >> 24) & 7u;
-  slot[cq.k] = (uint32_t)cq.q;
-  const bool mv = cq.qn >= 8u;
-  cq.q = mv ? cq.q >> 32 : cq.q;
-  cq.qn -= mv ? 8u : 0u;
-  cq.k += mv ? 1u : 0u;
+  const uint64_t c = (uint64_t)(ent & 0xFFFFFu) << cq.qs;
+  const uint32_t lo = cq.q | (uint32_t)c;
+  *(uint32_t*)(slot + cq.kb) = lo;
+  const uint32_t sum = cq.qs + ((ent >> 22) & 31u);
+  const bool mv = sum >= 32u;
+  cq.q = mv ? (uint32_t)(c >> 32) : lo;
+  cq.qs = sum & 31u;
+  cq.kb += mv ? 4u : 0u;
 }
 
 // Pipeline 2 and 3 store offset of chunk c's run 0 (bytes; run r adds
@@ -249,19 +251,21 @@ __device__ __forceinline__ void decode_codes(Src src, uint32_t base, int64_t ca,
   // raw rows of the brick: their codes are stored as zeros
   const uint32_t rawa = meta[ca >> 2].x;
   const uint32_t rawb = has_b ? meta[cb >> 2].x : 0u;
-  CodeQ qa = {0ull, 0u, 0u}, qb = {0ull, 0u, 0u};
+  CodeQ qa = {0u, 0u, 0u}, qb = {0u, 0u, 0u};
   const rsrc_t rs_out = make_rsrc(out, out_bytes);
   const uint32_t va = ilv_lane(ca, 8), vb = ilv_lane(cb, 8);
+  uint8_t* sa = (uint8_t*)slot_a;
+  uint8_t* sb = (uint8_t*)slot_b;
   for (int run = 0; run < 16; ++run) {
     for (int it = 0; it < 8; ++it) {
-      const bool take_a = qa.k < kCodeLead, take_b = qb.k < kCodeLead;
-      lookup_code(ba, qa, take_a, slot_a, lut);
-      lookup_code(bb, qb, take_b, slot_b, lut);
-      lookup_code(ba, qa, take_a, slot_a, lut);
-      lookup_code(bb, qb, take_b, slot_b, lut);
+      const bool take_a = qa.kb < 4 * kCodeLead, take_b = qb.kb < 4 * kCodeLead;
+      lookup_code(ba, qa, take_a, sa, lut);
+      lookup_code(bb, qb, take_b, sb, lut);
+      lookup_code(ba, qa, take_a, sa, lut);
+      lookup_code(bb, qb, take_b, sb, lut);
       refill(src, ba);
       refill(src, bb);
-      if (!__any(qa.k < 2u || qb.k < 2u)) break;
+      if (!__any(qa.kb < 8u || qb.kb < 8u)) break;
     }
     const uint32_t a0 = slot_a[0], a1 = slot_a[1], a2 = slot_a[2], a3 = slot_a[3];
     const uint32_t b0 = slot_b[0], b1 = slot_b[1], b2 = slot_b[2], b3 = slot_b[3];
@@ -269,8 +273,8 @@ __device__ __forceinline__ void decode_codes(Src src, uint32_t base, int64_t ca,
     slot_a[1] = a3;
     slot_b[0] = b2;
     slot_b[1] = b3;
-    qa.k -= 2u;
-    qb.k -= 2u;
+    qa.kb -= 8u;
+    qb.kb -= 8u;
     st8(rs_out, stored_codes(a0, a1, (rawa >> run) & 1u), va, (uint32_t)run * (8u * kChunksPerBlock));
     if (has_b) st8(rs_out, stored_codes(b0, b1, (rawb >> run) & 1u), vb, (uint32_t)run * (8u * kChunksPerBlock));
   }

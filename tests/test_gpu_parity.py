@@ -183,6 +183,26 @@ def test_rowk_fewer_bricks_than_waves(env, tokens):
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
 
 
+@pytest.mark.parametrize("tokens", [1, 3, 16])
+def test_gemv_odd_brick_count_and_short_waves(env, tokens):
+    """The LDS-activation GEMV on 27 bricks along K (an odd count: the
+    per-brick table copy is whole 4-byte pieces) and 34 brick-rows, every
+    gemv variant (8 or 16 waves: some waves own 1 or 2 bricks, fewer than the
+    bricks in flight), direct palette and runtime transcode, against fp64."""
+    torch, uw = env
+    w = synth.weights(544, 1728, 5, 0.003, 11)
+    x = synth.activations(tokens, 1728, xseed=9)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    names = uw.variants(tokens)
+    picked = [v for v, n in enumerate(names) if n.startswith("gemv")]
+    assert picked
+    for v in picked:
+        for p in (3, 4):
+            y = _run(env, m, x, p, variant=v)
+            assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
+
+
 def _raw_heavy_weights():
     """4 brick-rows x 4096 columns (1024 groups of 64 per brick-row) with raw
     groups forced by one exponent outside the palette per group (exponents
