@@ -17,6 +17,8 @@
 // groups, the raw side-table bytes, whose addresses come from the per-brick
 // table read one stage earlier still.  Partial sums meet in LDS; with
 // ksplit > 1 the slices add into a zeroed Y with float atomics.
+#include <algorithm>
+
 #include "kernels.h"
 #include "recon.h"
 
@@ -230,18 +232,19 @@ struct GStage {
   uint32_t before;  // wave-uniform raw groups before the brick
 };
 
+// One brick-row (brow) of one matrix: the body of the gemv kernels.
 template <int WAVES, int D, bool SIDE_LDS>
-__global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
+__device__ __forceinline__ void gemv_brick_row(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    uint64_t codes_bytes, int codes_ilv, int side_cap) {
+    uint64_t codes_bytes, int codes_ilv, int side_cap, uint32_t brow) {
   constexpr int R = D + 1;  // register stages
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int kbn = cols >> 6;
-  const uint32_t brick_row0 = blockIdx.x * (uint32_t)kbn;
+  const uint32_t brick_row0 = brow * (uint32_t)kbn;
   const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
   const rsrc_t rs_sm = make_rsrc(sm, nweights);
@@ -363,8 +366,31 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += red[w][k];
-    y[(size_t)tok * rows + (size_t)blockIdx.x * 16 + 4 * (l >> 4) + j] = sum;
+    y[(size_t)tok * rows + (size_t)brow * 16 + 4 * (l >> 4) + j] = sum;
   }
+}
+
+template <int WAVES, int D, bool SIDE_LDS>
+__global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
+    const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
+    const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
+    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
+    uint64_t codes_bytes, int codes_ilv, int side_cap) {
+  gemv_brick_row<WAVES, D, SIDE_LDS>(sm, codes, meta, side, side_bytes, lut0, lut1, lut2, lut3, x, y, tokens, rows,
+                                     cols, codes_bytes, codes_ilv, side_cap, blockIdx.x);
+}
+
+// Several matrices of one shape in one launch (the active experts of a
+// mixture-of-experts projection, each with its own rows of X and Y):
+// workgroup g takes brick-row g % (rows / 16) of job g / (rows / 16).  The
+// job table travels in the kernel arguments.
+template <int WAVES, int D, bool SIDE_LDS>
+__global__ __launch_bounds__(WAVES * 64) void fused_gemv_group_kernel(GemvGroup g, int rows, int cols, int side_cap) {
+  const uint32_t brows = (uint32_t)rows >> 4;
+  const uint32_t e = blockIdx.x / brows, brow = blockIdx.x - e * brows;
+  const GemvJob& j = g.job[e];
+  gemv_brick_row<WAVES, D, SIDE_LDS>(j.sm, j.codes, j.meta, j.side, j.side_bytes, j.lut[0], j.lut[1], j.lut[2],
+                                     j.lut[3], j.x, j.y, j.tokens, rows, cols, j.codes_bytes, 0, side_cap, brow);
 }
 
 template <int WAVES, int D>
@@ -381,6 +407,23 @@ hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tok
     hipLaunchKernelGGL((fused_gemv_kernel<WAVES, D, false>), dim3((unsigned)(w.rows / 16)), dim3(WAVES * 64), lds, s,
                        w.sm, w.codes, w.meta, w.side, w.side_bytes, w.lut[0], w.lut[1], w.lut[2], w.lut[3], x, y,
                        (int)tokens, (int)w.rows, (int)w.cols, w.codes_bytes, (int)w.codes_ilv, 0);
+  return hipGetLastError();
+}
+
+template <int WAVES, int D>
+hipError_t launch_gemv_group(const GemvGroup& g, int n, int64_t rows, int64_t cols, int64_t max_tokens,
+                             uint32_t max_row_raw, hipStream_t s) {
+  const bool side_lds = max_row_raw <= (uint32_t)kGemvSideCap;
+  const uint32_t cap = side_lds ? max_row_raw : 0u;
+  const size_t lds = kGemvX0 + gemv_xpad((uint32_t)(max_tokens * cols * 2)) + gemv_mpad((uint32_t)(cols / 64)) +
+                     (side_lds ? gemv_spad(cap) : 0u);
+  const dim3 grid((unsigned)(n * (rows / 16)));
+  if (side_lds)
+    hipLaunchKernelGGL((fused_gemv_group_kernel<WAVES, D, true>), grid, dim3(WAVES * 64), lds, s, g, (int)rows,
+                       (int)cols, (int)cap);
+  else
+    hipLaunchKernelGGL((fused_gemv_group_kernel<WAVES, D, false>), grid, dim3(WAVES * 64), lds, s, g, (int)rows,
+                       (int)cols, 0);
   return hipGetLastError();
 }
 
@@ -417,6 +460,40 @@ hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64
     return hipErrorInvalidValue;
 #define UW_CASE(W, D) \
   if (v.waves == W && v.unroll == D) return launch_gemv<W, D>(w, x, y, tokens, s);
+  UW_CASE(8, 2) UW_CASE(8, 1) UW_CASE(4, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)
+#undef UW_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys,
+                                   const int64_t* tokens, int n, const Variant& v, hipStream_t s) {
+  if (n < 1 || n > kGemvGroupMax) return hipErrorInvalidValue;
+  const int64_t rows = ws[0].rows, cols = ws[0].cols;
+  if (rows < 16 || rows % 16 || (rows / 16) * n > 0x7FFFFFFF) return hipErrorInvalidValue;
+  GemvGroup g = {};
+  int64_t max_tokens = 0;
+  uint32_t max_raw = 0;
+  for (int e = 0; e < n; ++e) {
+    const FusedW& w = ws[e];
+    if (w.rows != rows || w.cols != cols || w.exp_mode || w.codes_ilv || tokens[e] < 1 || tokens[e] > 16 ||
+        tokens[e] * cols > kGemvX || cols / 64 > kGemvKbn)
+      return hipErrorInvalidValue;
+    GemvJob& j = g.job[e];
+    j.sm = w.sm;
+    j.codes = w.codes;
+    j.meta = w.meta;
+    j.side = w.side;
+    j.side_bytes = w.side_bytes;
+    j.codes_bytes = w.codes_bytes;
+    for (int k = 0; k < 4; ++k) j.lut[k] = w.lut[k];
+    j.x = xs[e];
+    j.y = ys[e];
+    j.tokens = (int32_t)tokens[e];
+    max_tokens = std::max(max_tokens, tokens[e]);
+    max_raw = std::max(max_raw, w.max_row_raw);
+  }
+#define UW_CASE(W, D) \
+  if (v.waves == W && v.unroll == D) return launch_gemv_group<W, D>(g, n, rows, cols, max_tokens, max_raw, s);
   UW_CASE(8, 2) UW_CASE(8, 1) UW_CASE(4, 2) UW_CASE(16, 2) UW_CASE(8, 3) UW_CASE(4, 3)
 #undef UW_CASE
   return hipErrorInvalidValue;

@@ -37,6 +37,8 @@ struct Variant {
 int variant_count(int64_t tokens);
 bool variant_get(int64_t tokens, int id, Variant* v);  // id 0 = default for (tokens, shape)
 Variant variant_default(int64_t tokens, int64_t rows, int64_t cols);
+// The default gemv variant (the one the default picks where gemv applies).
+Variant variant_gemv();
 // The variant that actually launches for v (a choice that does not apply to
 // the shape or form falls back to the default of its family).
 Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_mode, const Variant& v);
@@ -59,6 +61,29 @@ void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len);
 
 hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                         hipStream_t s);
+
+// One gemv launch over n <= kGemvGroupMax palette-form matrices of one shape
+// (pipeline 4, each with its own activations, outputs and 1..16 tokens that
+// fit the gemv variants); v is a gemv variant (kind 2).
+constexpr int kGemvGroupMax = 16;
+struct GemvJob {
+  const uint8_t* sm;
+  const uint8_t* codes;
+  const uint2* meta;
+  const uint8_t* side;
+  uint64_t side_bytes;
+  uint64_t codes_bytes;
+  uint32_t lut[4];
+  const uint16_t* x;
+  float* y;
+  int32_t tokens;
+  int32_t pad;
+};
+struct GemvGroup {
+  GemvJob job[kGemvGroupMax];
+};
+hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys,
+                                   const int64_t* tokens, int n, const Variant& v, hipStream_t s);
 
 // Huffman decode of every chunk (one lane per 256-symbol chunk).
 enum DecodeEmit { EMIT_BF16 = 0, EMIT_EXP = 1, EMIT_NIBBLE = 2 };

@@ -1182,13 +1182,78 @@ uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t*
     if (st != UW_OK) return st;
   }
   const int64_t rows = experts[0]->rows, cols = experts[0]->cols;
+  // Experts whose call resolves to pipeline 4 with few enough tokens for the
+  // gemv kernels go out together, up to kGemvGroupMax per launch, on the
+  // stream of the first of them: those whose variant is a gemv one, and those
+  // left to the default when the group's brick-rows fill the chip (a single
+  // short matrix takes the K-split small kernel by default; a group of them
+  // does not need it).  Every other expert runs one launch of its own.
+  const int64_t kbn = cols / 64, brows = rows / 16;
+  struct Call {
+    int p = 0, var = 0;
+    uw::Variant v{}, ev{};
+    bool cand = false;
+  };
+  std::vector<Call> calls(n);
+  int64_t cand_brows = 0;
   for (int32_t e = 0; e < n; ++e) {
     const int64_t t = row_offsets[e + 1] - row_offsets[e];
     if (t == 0) continue;
-    uw_status st = matmul_impl(experts[e], x_dev + row_offsets[e] * cols, y_dev + row_offsets[e] * rows, t, pipeline);
+    Call& c = calls[e];
+    uw_status st = matmul_check(experts[e], x_dev, y_dev, t, pipeline, &c.p, &c.v);
     if (st != UW_OK) return st;
+    (void)resolve_pipeline(experts[e], t, pipeline, &c.var);
+    if (c.p != 4) continue;
+    c.ev = uw::variant_effective(t, rows, cols, false, c.v);
+    const bool fits = t <= 16 && t * cols <= uw::kGemvXElems && kbn <= uw::kGemvKbnMax;
+    c.cand = c.ev.kind == 2 || (c.var == 0 && fits);
+    if (c.cand) cand_brows += brows;
   }
-  return UW_OK;
+  uw::FusedW gw[uw::kGemvGroupMax];
+  const uint16_t* gx[uw::kGemvGroupMax];
+  float* gy[uw::kGemvGroupMax];
+  int64_t gt[uw::kGemvGroupMax];
+  int ng = 0;
+  bool have_group = false;
+  uw::Variant gv{};
+  hipStream_t gs = nullptr;
+  auto flush = [&]() -> uw_status {
+    if (ng == 0) return UW_OK;
+    UW_HIP(uw::launch_fused_gemv_group(gw, gx, gy, gt, ng, gv, gs));
+    ng = 0;
+    return UW_OK;
+  };
+  for (int32_t e = 0; e < n; ++e) {
+    const int64_t t = row_offsets[e + 1] - row_offsets[e];
+    if (t == 0) continue;
+    const uint16_t* xe = x_dev + row_offsets[e] * cols;
+    float* ye = y_dev + row_offsets[e] * rows;
+    const Call& c = calls[e];
+    // the variant this expert would run in a group
+    uw::Variant mine = c.ev;
+    if (c.cand && c.ev.kind != 2) mine = cand_brows >= 128 ? uw::variant_gemv() : c.ev;
+    const bool joins = c.cand && mine.kind == 2 &&
+                       (!have_group || (experts[e]->main == gs && mine.waves == gv.waves && mine.unroll == gv.unroll));
+    if (!joins) {
+      uw_status st = matmul_impl(experts[e], xe, ye, t, pipeline);
+      if (st != UW_OK) return st;
+      continue;
+    }
+    if (!have_group) {
+      have_group = true;
+      gv = mine;
+      gs = experts[e]->main;
+    }
+    gw[ng] = fused_view(experts[e], false, experts[e]->d_nib);
+    gx[ng] = xe;
+    gy[ng] = ye;
+    gt[ng] = t;
+    if (++ng == uw::kGemvGroupMax) {
+      uw_status st = flush();
+      if (st != UW_OK) return st;
+    }
+  }
+  return flush();
 }
 
 void uw_free(uw_handle h) {

@@ -141,6 +141,8 @@ Variant small_default(int64_t tokens, int64_t rows, int64_t cols) {
 
 }  // namespace
 
+Variant variant_gemv() { return Variant{2, 8, 1, 2, 0}; }
+
 Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   const int64_t brows = rows / 16, kbn = cols / 64;
   if (tokens <= 64) {
@@ -150,8 +152,7 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
     // (8 waves per brick-row, two bricks in flight while one is computed:
     // measured best or within 1% on 14336x4096, 4096x14336, 28672x8192 and
     // 128256x4096 at one token)
-    if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128)
-      return Variant{2, 8, 1, 2, 0};
+    if (tokens <= 16 && tokens * cols <= kGemvXElems && kbn <= kGemvKbnMax && brows >= 128) return variant_gemv();
     // from 12 tokens (20 for matrices too short to fill the chip without a
     // K split): four brick-rows per workgroup over the whole of K, the
     // activations streamed through LDS in 8-brick slices

@@ -255,8 +255,12 @@ uw_status uw_evict(uw_handle h);
  * by expert by the caller) times expert e's W^T into the same rows of Y.
  * x_dev: [row_offsets[n], cols] bf16, y_dev: [row_offsets[n], rows] fp32,
  * row_offsets: host, n+1 non-decreasing entries from 0.  All experts share one
- * shape and must be on the device; each expert's kernels go to its own main
- * stream, in expert order; experts without rows are skipped.  Errors:
+ * shape and must be on the device; experts without rows are skipped.  Experts
+ * whose call resolves to the direct-palette gemv kernels (pipeline 4, few
+ * tokens) with the same variant and main stream as the first such expert run
+ * together, up to 16 per kernel launch, on that stream (the Unweight page,
+ * section 十一: cold experts); every other expert's kernels go to its own main
+ * stream, in expert order.  Errors:
  * UW_ERR_INVALID_ARG, UW_ERR_SHAPE (experts differ), UW_ERR_UNSUPPORTED (an
  * expert is host-only or lacks the pipeline's format), as for uw_matmul. */
 uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t* x_dev, const int64_t* row_offsets,

@@ -76,3 +76,44 @@ def test_grouped_matmul(env, pipeline):
             continue
         ref = oracle.matmul_fp64(xb[offs[e]:offs[e + 1]], ws[e])
         assert oracle.rel_err(yh[offs[e]:offs[e + 1]], ref) <= TOL, e
+
+
+def test_grouped_gemv_launch(env):
+    """More active experts than one grouped gemv launch holds, with short
+    matrices (17 brick-rows, 9 bricks of K): the experts that fit the gemv
+    kernels share launches, the one with 20 tokens runs alone.  Each expert is
+    checked against fp64 and, bit for bit, against a single-matrix call forced
+    to the same gemv variant (same kernel body, same summation order)."""
+    torch, uw = env
+    rows, cols, n = 272, 576, 22
+    ws = [synth.weights(rows, cols, 300 + e, 0.003, 11) for e in range(n)]
+    experts = [uw.Matrix(w, uw.FMT_PALETTE | uw.ENC_HOST_ONLY) for w in ws]
+    for m in experts:
+        m.upload()
+    counts = [1, 2, 0, 1, 3, 1, 1, 16, 1, 0, 2, 1, 1, 1, 20, 1, 4, 1, 1, 2, 1, 1]
+    assert len(counts) == n
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    xb = synth.activations(int(offs[-1]), cols, xseed=17)
+    x = uw.bf16_tensor(xb)
+    y = torch.full((int(offs[-1]), rows), float("nan"), device="cuda", dtype=torch.float32)
+    print("grouped gemv: 22 experts", flush=True)
+    uw.grouped_matmul(experts, x, y, offs, 4)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    for e in range(n):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        ref = oracle.matmul_fp64(xb[a:b], ws[e])
+        assert oracle.rel_err(yh[a:b], ref) <= TOL, e
+        if counts[e] > 16:
+            continue
+        names = uw.variants(counts[e])
+        experts[e].set_variant(names.index("gemv:w8:d2"))
+        ys = torch.full((b - a, rows), float("nan"), device="cuda", dtype=torch.float32)
+        experts[e].matmul(x[a:b], ys, pipeline=4)
+        torch.cuda.synchronize()
+        experts[e].set_variant(0)
+        assert np.array_equal(ys.cpu().numpy(), yh[a:b]), e
+    for m in experts:
+        m.free()
