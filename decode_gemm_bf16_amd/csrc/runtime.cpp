@@ -693,23 +693,36 @@ uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, cons
     return fail(UW_ERR_INVALID_ARG, "workspace of %zu bytes, %lld tokens need %zu", work_bytes, (long long)tokens,
                 uw_mlp_workspace_bytes(tokens, inter));
   uw_matrix* const hs[3] = {gate, up, down};
+  int ps[3] = {0, 0, 0};
+  Variant vs[3];
   for (int j = 0; j < 3; ++j) {
-    int p = 0;
-    Variant v;
     // x_dev stands in for each projection's input: only non-null is checked
-    uw_status st = matmul_check(hs[j], x_dev, y_dev, tokens, pipelines[j], &p, &v);
+    uw_status st = matmul_check(hs[j], x_dev, y_dev, tokens, pipelines[j], &ps[j], &vs[j]);
     if (st != UW_OK) return st;
-    if (fused_only && p != 4)
+    if (fused_only && ps[j] != 4)
       return fail(UW_ERR_UNSUPPORTED, "projection %d resolves to pipeline %d; only pipeline 4 runs without allocating",
-                  j, p);
+                  j, ps[j]);
   }
   uint8_t* cur = static_cast<uint8_t*>(work_dev);
   float* g = carve<float>(cur, size_t(tokens) * inter * 4);
   float* u = carve<float>(cur, size_t(tokens) * inter * 4);
   uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
   uw_status st;
-  if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
-  if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;
+  // gate and up read the same activations: when both take the same
+  // direct-palette gemv variant they go out as one launch (one ramp and
+  // drain of the HBM stream instead of two)
+  const Variant eg = ps[0] == 4 ? variant_effective(tokens, inter, hidden, false, vs[0]) : vs[0];
+  const Variant eu = ps[1] == 4 ? variant_effective(tokens, inter, hidden, false, vs[1]) : vs[1];
+  if (ps[0] == 4 && ps[1] == 4 && eg.kind == 2 && eu.kind == 2 && eg.waves == eu.waves && eg.unroll == eu.unroll) {
+    const FusedW ws[2] = {fused_view(gate, false, gate->d_nib), fused_view(up, false, up->d_nib)};
+    const uint16_t* xs[2] = {x_dev, x_dev};
+    float* ys[2] = {g, u};
+    const int64_t ts[2] = {tokens, tokens};
+    UW_HIP(launch_fused_gemv_group(ws, xs, ys, ts, 2, eg, gate->main));
+  } else {
+    if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
+    if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;
+  }
   UW_HIP(launch_silu_mul(g, u, hh, tokens * inter, gate->main));
   return matmul_impl(down, hh, y_dev, tokens, pipelines[2]);
 }

@@ -363,6 +363,40 @@ def test_mlp_layer_8b_shapes(env, pipes):
         assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL, (tokens, oracle.rel_err(y.cpu().numpy(), ref))
 
 
+def test_mlp_forward_gate_up_one_launch(env):
+    """gate and up take the same gemv variant, so uw_mlp_forward sends them
+    out as one launch: the layer must equal, bit for bit, the same layer run
+    as separate calls (gate, up, silu*mul, down), and the fp64 layer."""
+    torch, uw = env
+    hidden, inter = 1024, 2048  # 128 brick-rows: the gemv kernels are the default
+    ws = [synth.weights(inter, hidden, 60, 0.002, 10), synth.weights(inter, hidden, 61, 0.002, 10),
+          synth.weights(hidden, inter, 62, 0.002, 10)]
+    mats = [_both(env, w) for w in ws]
+    # the down projection (64 brick-rows) would split K with atomic sums by
+    # default; variant 1 does not, so both runs add in one order
+    mats[2].set_variant(1)
+    work = torch.empty(uw.mlp_workspace_bytes(16, inter), dtype=torch.uint8, device="cuda")
+    for tokens in (1, 5, 16):
+        print(f"gate+up one launch, tokens {tokens}", flush=True)
+        assert mats[0].variant_in_use(tokens, 4)[1].startswith("gemv"), mats[0].variant_in_use(tokens, 4)
+        x = synth.activations(tokens, hidden, xseed=30 + tokens)
+        xd = uw.bf16_tensor(x)
+        y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        uw.mlp_forward(*mats, [4, 4, 4], xd, y, tokens, work)
+        g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
+        u = torch.empty_like(g)
+        h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
+        y2 = torch.empty_like(y)
+        mats[0].matmul(xd, g, tokens, 4)
+        mats[1].matmul(xd, u, tokens, 4)
+        uw.silu_mul(g, u, h)
+        mats[2].matmul(h, y2, tokens, 4)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), y2.cpu().numpy()), tokens
+        _, _, _, ref = oracle.mlp_layer_fp64(x, *ws)
+        assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL, tokens
+
+
 def test_silu_mul(env):
     torch, uw = env
     rng = np.random.default_rng(4)
