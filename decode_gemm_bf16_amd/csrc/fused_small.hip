@@ -390,7 +390,7 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_group_kernel(GemvGroup 
   const uint32_t e = blockIdx.x / brows, brow = blockIdx.x - e * brows;
   const GemvJob& j = g.job[e];
   gemv_brick_row<WAVES, D, SIDE_LDS>(j.sm, j.codes, j.meta, j.side, j.side_bytes, j.lut[0], j.lut[1], j.lut[2],
-                                     j.lut[3], j.x, j.y, j.tokens, rows, cols, j.codes_bytes, 0, side_cap, brow);
+                                     j.lut[3], j.x, j.y, j.tokens, rows, cols, j.codes_bytes, j.codes_ilv, side_cap, brow);
 }
 
 template <int WAVES, int D>
@@ -475,7 +475,7 @@ hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, 
   uint32_t max_raw = 0;
   for (int e = 0; e < n; ++e) {
     const FusedW& w = ws[e];
-    if (w.rows != rows || w.cols != cols || w.exp_mode || w.codes_ilv || tokens[e] < 1 || tokens[e] > 16 ||
+    if (w.rows != rows || w.cols != cols || w.exp_mode || tokens[e] < 1 || tokens[e] > 16 ||
         tokens[e] * cols > kGemvX || cols / 64 > kGemvKbn)
       return hipErrorInvalidValue;
     GemvJob& j = g.job[e];
@@ -489,6 +489,7 @@ hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, 
     j.x = xs[e];
     j.y = ys[e];
     j.tokens = (int32_t)tokens[e];
+    j.codes_ilv = w.codes_ilv ? 1 : 0;
     max_tokens = std::max(max_tokens, tokens[e]);
     max_raw = std::max(max_raw, w.max_row_raw);
   }

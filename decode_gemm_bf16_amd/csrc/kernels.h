@@ -62,9 +62,10 @@ void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len);
 hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                         hipStream_t s);
 
-// One gemv launch over n <= kGemvGroupMax palette-form matrices of one shape
-// (pipeline 4, each with its own activations, outputs and 1..16 tokens that
-// fit the gemv variants); v is a gemv variant (kind 2).
+// One gemv launch over n <= kGemvGroupMax matrices of one shape in the
+// palette form or as 4-bit codes in scratch (pipelines 4 and 3), each with its
+// own activations, outputs and 1..16 tokens that fit the gemv variants; v is
+// a gemv variant (kind 2).
 constexpr int kGemvGroupMax = 16;
 struct GemvJob {
   const uint8_t* sm;
@@ -77,7 +78,7 @@ struct GemvJob {
   const uint16_t* x;
   float* y;
   int32_t tokens;
-  int32_t pad;
+  int32_t codes_ilv;  // codes in the interleaved scratch order
 };
 struct GemvGroup {
   GemvJob job[kGemvGroupMax];

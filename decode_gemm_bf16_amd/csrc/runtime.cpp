@@ -708,17 +708,28 @@ uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, cons
   float* u = carve<float>(cur, size_t(tokens) * inter * 4);
   uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
   uw_status st;
-  // gate and up read the same activations: when both take the same
-  // direct-palette gemv variant they go out as one launch (one ramp and
-  // drain of the HBM stream instead of two)
-  const Variant eg = ps[0] == 4 ? variant_effective(tokens, inter, hidden, false, vs[0]) : vs[0];
-  const Variant eu = ps[1] == 4 ? variant_effective(tokens, inter, hidden, false, vs[1]) : vs[1];
-  if (ps[0] == 4 && ps[1] == 4 && eg.kind == 2 && eu.kind == 2 && eg.waves == eu.waves && eg.unroll == eu.unroll) {
-    const FusedW ws[2] = {fused_view(gate, false, gate->d_nib), fused_view(up, false, up->d_nib)};
+  // gate and up read the same activations: when both run the same gemv
+  // variant on 4-bit codes -- the palette form (pipeline 4) or codes decoded
+  // into scratch (pipeline 3, separate scratch buffers) -- they go out as one
+  // launch (one ramp and drain of the HBM stream instead of two)
+  const bool codes = ps[0] == ps[1] && (ps[0] == 4 || ps[0] == 3);
+  const Variant eg = codes ? variant_effective(tokens, inter, hidden, false, vs[0]) : vs[0];
+  const Variant eu = codes ? variant_effective(tokens, inter, hidden, false, vs[1]) : vs[1];
+  bool group = codes && eg.kind == 2 && eu.kind == 2 && eg.waves == eu.waves && eg.unroll == eu.unroll;
+  if (group && ps[0] == 3) {
+    if ((st = ensure_scratch(gate, 3)) != UW_OK || (st = ensure_scratch(up, 3)) != UW_OK) return st;
+    group = gate->scratch != up->scratch;
+  }
+  if (group) {
+    const bool p3 = ps[0] == 3;
+    if (p3 && ((st = prepare(gate, 3)) != UW_OK || (st = prepare(up, 3)) != UW_OK)) return st;
+    const FusedW ws[2] = {fused_view(gate, false, p3 ? (const uint8_t*)gate->scratch : gate->d_nib),
+                          fused_view(up, false, p3 ? (const uint8_t*)up->scratch : up->d_nib)};
     const uint16_t* xs[2] = {x_dev, x_dev};
     float* ys[2] = {g, u};
     const int64_t ts[2] = {tokens, tokens};
     UW_HIP(launch_fused_gemv_group(ws, xs, ys, ts, 2, eg, gate->main));
+    if (p3 && ((st = mark_consumed(gate)) != UW_OK || (st = mark_consumed(up)) != UW_OK)) return st;
   } else {
     if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
     if ((st = matmul_impl(up, x_dev, u, tokens, pipelines[1])) != UW_OK) return st;

@@ -363,10 +363,12 @@ def test_mlp_layer_8b_shapes(env, pipes):
         assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL, (tokens, oracle.rel_err(y.cpu().numpy(), ref))
 
 
-def test_mlp_forward_gate_up_one_launch(env):
-    """gate and up take the same gemv variant, so uw_mlp_forward sends them
-    out as one launch: the layer must equal, bit for bit, the same layer run
-    as separate calls (gate, up, silu*mul, down), and the fp64 layer."""
+@pytest.mark.parametrize("gu", [4, 3])
+def test_mlp_forward_gate_up_one_launch(env, gu):
+    """gate and up take the same gemv variant (on the palette form, pipeline
+    4, or on codes decoded into scratch, pipeline 3), so uw_mlp_forward sends
+    them out as one launch: the layer must equal, bit for bit, the same layer
+    run as separate calls (gate, up, silu*mul, down), and the fp64 layer."""
     torch, uw = env
     hidden, inter = 1024, 2048  # 128 brick-rows: the gemv kernels are the default
     ws = [synth.weights(inter, hidden, 60, 0.002, 10), synth.weights(inter, hidden, 61, 0.002, 10),
@@ -377,18 +379,18 @@ def test_mlp_forward_gate_up_one_launch(env):
     mats[2].set_variant(1)
     work = torch.empty(uw.mlp_workspace_bytes(16, inter), dtype=torch.uint8, device="cuda")
     for tokens in (1, 5, 16):
-        print(f"gate+up one launch, tokens {tokens}", flush=True)
-        assert mats[0].variant_in_use(tokens, 4)[1].startswith("gemv"), mats[0].variant_in_use(tokens, 4)
+        print(f"gate+up one launch, pipeline {gu}, tokens {tokens}", flush=True)
+        assert mats[0].variant_in_use(tokens, gu)[1].startswith("gemv"), mats[0].variant_in_use(tokens, gu)
         x = synth.activations(tokens, hidden, xseed=30 + tokens)
         xd = uw.bf16_tensor(x)
         y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
-        uw.mlp_forward(*mats, [4, 4, 4], xd, y, tokens, work)
+        uw.mlp_forward(*mats, [gu, gu, 4], xd, y, tokens, work)
         g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
         u = torch.empty_like(g)
         h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
         y2 = torch.empty_like(y)
-        mats[0].matmul(xd, g, tokens, 4)
-        mats[1].matmul(xd, u, tokens, 4)
+        mats[0].matmul(xd, g, tokens, gu)
+        mats[1].matmul(xd, u, tokens, gu)
         uw.silu_mul(g, u, h)
         mats[2].matmul(h, y2, tokens, 4)
         torch.cuda.synchronize()
