@@ -37,12 +37,13 @@ struct KStage {
 
 constexpr size_t kRowkLdsBytes = 160 * 1024;  // one workgroup may take a whole CU's LDS
 
+// Row group rg (brick-rows rg*R ..) of one matrix: the body of the kernels.
 template <int R, int P, int U, int D, int TB, bool EXPM>
-__global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
+__device__ __forceinline__ void rowk_row_group(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
     uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
-    int kper, int ksplit, uint64_t codes_bytes, int codes_ilv) {
+    int kper, int ksplit, uint64_t codes_bytes, int codes_ilv, int rg) {
   constexpr int WAVES = R * P, NT = WAVES * 64, S = P * U;
   static_assert(D % U == 0, "ring stages must repeat every D / U slices");
   constexpr int SL = D / U;  // slices per unrolled loop step
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
   // K range of the workgroup (the whole of K unless the grid splits it):
   // bricks [kb0, kb0 + nkb), a multiple of S long except the last
   const int kb0 = blockIdx.y * kper, nkb = min(kper, kbn - kb0);
-  const int brow = blockIdx.x * R + rw;
+  const int brow = rg * R + rw;
   const bool has_row = brow < brows;
   const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
   const uint32_t nweights = (uint32_t)rows * (uint32_t)cols;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
   issue_x(0);
   if (!EXPM) {
     for (int i = threadIdx.x; i < R * kper; i += NT) {
-      const int br = blockIdx.x * R + i / kper, kk = i % kper;
+      const int br = rg * R + i / kper, kk = i % kper;
       ms[i] = br < brows && kk < nkb ? meta[(size_t)br * kbn + kb0 + kk] : uint2{0u, 0u};
     }
   }
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
     }
   }
   __syncthreads();
-  const int row0 = blockIdx.x * WR;
+  const int row0 = rg * WR;
   const int nrow = min(WR, rows - row0);
   for (int e = threadIdx.x; e < tokens * WR; e += NT) {
     const int tok = e / WR, rr = e - tok * WR;
@@ -245,6 +246,39 @@ __global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
     else
       unsafeAtomicAdd(y + (size_t)tok * rows + row0 + rr, v);
   }
+}
+
+template <int R, int P, int U, int D, int TB, bool EXPM>
+__global__ __launch_bounds__(R * P * 64) void fused_rowk_kernel(
+    const uint8_t* __restrict__ sm, const uint8_t* __restrict__ codes, const uint2* __restrict__ meta,
+    const uint8_t* __restrict__ side, uint64_t side_bytes, uint32_t lut0, uint32_t lut1, uint32_t lut2,
+    uint32_t lut3, const uint16_t* __restrict__ x, float* __restrict__ y, int tokens, int rows, int cols,
+    int kper, int ksplit, uint64_t codes_bytes, int codes_ilv) {
+  rowk_row_group<R, P, U, D, TB, EXPM>(sm, codes, meta, side, side_bytes, lut0, lut1, lut2, lut3, x, y, tokens, rows,
+                                       cols, kper, ksplit, codes_bytes, codes_ilv, blockIdx.x);
+}
+
+// Several matrices of one shape and token count in one launch (gate and up
+// of a layer): workgroup (g, k) takes row group g % ngroups of job
+// g / ngroups, K range k.  The job table travels in the kernel arguments.
+template <int R, int P, int U, int D, int TB>
+__global__ __launch_bounds__(R * P * 64) void fused_rowk_group_kernel(FusedGroup g, int tokens, int rows, int cols,
+                                                                      int kper, int ksplit, int ngroups) {
+  const int e = blockIdx.x / ngroups, rg = blockIdx.x - e * ngroups;
+  const FusedJob& j = g.job[e];
+  rowk_row_group<R, P, U, D, TB, false>(j.sm, j.codes, j.meta, j.side, j.side_bytes, j.lut[0], j.lut[1], j.lut[2],
+                                        j.lut[3], j.x, j.y, tokens, rows, cols, kper, ksplit, j.codes_bytes,
+                                        j.codes_ilv, rg);
+}
+
+template <int R, int P, int U, int D, int TB>
+hipError_t launch_rowk_group_t(const FusedGroup& g, int n, int64_t tokens, int64_t rows, int64_t cols, int kper,
+                               int ksplit, size_t lds, hipStream_t s) {
+  const int ngroups = (int)((rows / 16 + R - 1) / R);
+  const dim3 grid((unsigned)(n * ngroups), (unsigned)ksplit);
+  hipLaunchKernelGGL((fused_rowk_group_kernel<R, P, U, D, TB>), grid, dim3(R * P * 64), lds, s, g, (int)tokens,
+                     (int)rows, (int)cols, kper, ksplit, ngroups);
+  return hipGetLastError();
 }
 
 template <int R, int P, int U, int D, int TB>
@@ -323,6 +357,52 @@ bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v) {
   // above 64 tokens only the R4 P4 U1 and R4 P2 U2 shapes are built
   if (tokens > 64 && tokens <= 128 && !big_shape(v)) return false;
   return rowk_plan(tokens, rows, cols, v, nullptr, nullptr) <= kRowkLdsBytes;
+}
+
+hipError_t launch_fused_rowk_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys, int n,
+                                   int64_t tokens, const Variant& v, hipStream_t s) {
+  if (n < 1 || n > kFusedGroupMax || tokens < 1 || tokens > 64) return hipErrorInvalidValue;
+  const int64_t rows = ws[0].rows, cols = ws[0].cols;
+  if (!rowk_fits(tokens, rows, cols, v)) return hipErrorInvalidValue;
+  const int R = v.tile, P = v.waves, U = v.ksplit, D = v.unroll;
+  int kper = 0, ks = 0;
+  const size_t lds = rowk_plan(tokens, rows, cols, v, &kper, &ks);
+  if (lds > kRowkLdsBytes || (int64_t)n * ((rows / 16 + R - 1) / R) > 0x7FFFFFFF) return hipErrorInvalidValue;
+  FusedGroup g = {};
+  for (int e = 0; e < n; ++e) {
+    const FusedW& w = ws[e];
+    if (w.rows != rows || w.cols != cols || w.exp_mode) return hipErrorInvalidValue;
+    FusedJob& j = g.job[e];
+    j.sm = w.sm;
+    j.codes = w.codes;
+    j.meta = w.meta;
+    j.side = w.side;
+    j.side_bytes = w.side_bytes;
+    j.codes_bytes = w.codes_bytes;
+    for (int k = 0; k < 4; ++k) j.lut[k] = w.lut[k];
+    j.x = xs[e];
+    j.y = ys[e];
+    j.tokens = (int32_t)tokens;
+    j.codes_ilv = w.codes_ilv ? 1 : 0;
+  }
+  if (ks > 1) {
+    for (int e = 0; e < n; ++e) {
+      hipError_t err = launch_zero(ys[e], tokens * rows, s);
+      if (err != hipSuccess) return err;
+    }
+  }
+#define UW_CASE(RR, PP, UU, DD)                                                                          \
+  if (R == RR && P == PP && U == UU && D == DD) {                                                        \
+    switch ((tokens + 15) / 16) {                                                                        \
+      case 1: return launch_rowk_group_t<RR, PP, UU, DD, 1>(g, n, tokens, rows, cols, kper, ks, lds, s); \
+      case 2: return launch_rowk_group_t<RR, PP, UU, DD, 2>(g, n, tokens, rows, cols, kper, ks, lds, s); \
+      case 3: return launch_rowk_group_t<RR, PP, UU, DD, 3>(g, n, tokens, rows, cols, kper, ks, lds, s); \
+      default: return launch_rowk_group_t<RR, PP, UU, DD, 4>(g, n, tokens, rows, cols, kper, ks, lds, s); \
+    }                                                                                                    \
+  }
+  UW_CASE(4, 4, 2, 2) UW_CASE(4, 2, 2, 2)
+#undef UW_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused_rowk(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,

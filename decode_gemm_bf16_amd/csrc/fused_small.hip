@@ -385,10 +385,10 @@ __global__ __launch_bounds__(WAVES * 64) void fused_gemv_kernel(
 // workgroup g takes brick-row g % (rows / 16) of job g / (rows / 16).  The
 // job table travels in the kernel arguments.
 template <int WAVES, int D, bool SIDE_LDS>
-__global__ __launch_bounds__(WAVES * 64) void fused_gemv_group_kernel(GemvGroup g, int rows, int cols, int side_cap) {
+__global__ __launch_bounds__(WAVES * 64) void fused_gemv_group_kernel(FusedGroup g, int rows, int cols, int side_cap) {
   const uint32_t brows = (uint32_t)rows >> 4;
   const uint32_t e = blockIdx.x / brows, brow = blockIdx.x - e * brows;
-  const GemvJob& j = g.job[e];
+  const FusedJob& j = g.job[e];
   gemv_brick_row<WAVES, D, SIDE_LDS>(j.sm, j.codes, j.meta, j.side, j.side_bytes, j.lut[0], j.lut[1], j.lut[2],
                                      j.lut[3], j.x, j.y, j.tokens, rows, cols, j.codes_bytes, j.codes_ilv, side_cap, brow);
 }
@@ -411,7 +411,7 @@ hipError_t launch_gemv(const FusedW& w, const uint16_t* x, float* y, int64_t tok
 }
 
 template <int WAVES, int D>
-hipError_t launch_gemv_group(const GemvGroup& g, int n, int64_t rows, int64_t cols, int64_t max_tokens,
+hipError_t launch_gemv_group(const FusedGroup& g, int n, int64_t rows, int64_t cols, int64_t max_tokens,
                              uint32_t max_row_raw, hipStream_t s) {
   const bool side_lds = max_row_raw <= (uint32_t)kGemvSideCap;
   const uint32_t cap = side_lds ? max_row_raw : 0u;
@@ -467,10 +467,10 @@ hipError_t launch_fused_gemv(const FusedW& w, const uint16_t* x, float* y, int64
 
 hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys,
                                    const int64_t* tokens, int n, const Variant& v, hipStream_t s) {
-  if (n < 1 || n > kGemvGroupMax) return hipErrorInvalidValue;
+  if (n < 1 || n > kFusedGroupMax) return hipErrorInvalidValue;
   const int64_t rows = ws[0].rows, cols = ws[0].cols;
   if (rows < 16 || rows % 16 || (rows / 16) * n > 0x7FFFFFFF) return hipErrorInvalidValue;
-  GemvGroup g = {};
+  FusedGroup g = {};
   int64_t max_tokens = 0;
   uint32_t max_raw = 0;
   for (int e = 0; e < n; ++e) {
@@ -478,7 +478,7 @@ hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, 
     if (w.rows != rows || w.cols != cols || w.exp_mode || tokens[e] < 1 || tokens[e] > 16 ||
         tokens[e] * cols > kGemvX || cols / 64 > kGemvKbn)
       return hipErrorInvalidValue;
-    GemvJob& j = g.job[e];
+    FusedJob& j = g.job[e];
     j.sm = w.sm;
     j.codes = w.codes;
     j.meta = w.meta;

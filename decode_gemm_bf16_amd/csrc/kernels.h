@@ -62,12 +62,12 @@ void variant_describe(int64_t tokens, const Variant& v, char* buf, size_t len);
 hipError_t launch_fused(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                         hipStream_t s);
 
-// One gemv launch over n <= kGemvGroupMax matrices of one shape in the
+// One gemv launch over n <= kFusedGroupMax matrices of one shape in the
 // palette form or as 4-bit codes in scratch (pipelines 4 and 3), each with its
 // own activations, outputs and 1..16 tokens that fit the gemv variants; v is
 // a gemv variant (kind 2).
-constexpr int kGemvGroupMax = 16;
-struct GemvJob {
+constexpr int kFusedGroupMax = 16;
+struct FusedJob {
   const uint8_t* sm;
   const uint8_t* codes;
   const uint2* meta;
@@ -80,11 +80,16 @@ struct GemvJob {
   int32_t tokens;
   int32_t codes_ilv;  // codes in the interleaved scratch order
 };
-struct GemvGroup {
-  GemvJob job[kGemvGroupMax];
+struct FusedGroup {
+  FusedJob job[kFusedGroupMax];
 };
 hipError_t launch_fused_gemv_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys,
                                    const int64_t* tokens, int n, const Variant& v, hipStream_t s);
+// The same for the whole-K variants (kind 4, the R4 P4 U2 D2 and R4 P2 U2 D2
+// shapes, 1..64 tokens), all n matrices with `tokens` tokens; the palette form
+// or 4-bit codes in scratch.
+hipError_t launch_fused_rowk_group(const FusedW* ws, const uint16_t* const* xs, float* const* ys, int n,
+                                   int64_t tokens, const Variant& v, hipStream_t s);
 
 // Huffman decode of every chunk (one lane per 256-symbol chunk).
 enum DecodeEmit { EMIT_BF16 = 0, EMIT_EXP = 1, EMIT_NIBBLE = 2 };

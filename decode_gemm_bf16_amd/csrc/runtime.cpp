@@ -708,14 +708,18 @@ uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, cons
   float* u = carve<float>(cur, size_t(tokens) * inter * 4);
   uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
   uw_status st;
-  // gate and up read the same activations: when both run the same gemv
-  // variant on 4-bit codes -- the palette form (pipeline 4) or codes decoded
-  // into scratch (pipeline 3, separate scratch buffers) -- they go out as one
-  // launch (one ramp and drain of the HBM stream instead of two)
+  // gate and up read the same activations: when both run the same gemv or
+  // whole-K variant on 4-bit codes -- the palette form (pipeline 4) or codes
+  // decoded into scratch (pipeline 3, separate scratch buffers) -- they go out
+  // as one launch (one ramp and drain of the HBM stream instead of two)
   const bool codes = ps[0] == ps[1] && (ps[0] == 4 || ps[0] == 3);
   const Variant eg = codes ? variant_effective(tokens, inter, hidden, false, vs[0]) : vs[0];
   const Variant eu = codes ? variant_effective(tokens, inter, hidden, false, vs[1]) : vs[1];
-  bool group = codes && eg.kind == 2 && eu.kind == 2 && eg.waves == eu.waves && eg.unroll == eu.unroll;
+  const bool same = eg.kind == eu.kind && eg.waves == eu.waves && eg.ksplit == eu.ksplit &&
+                    eg.unroll == eu.unroll && eg.tile == eu.tile;
+  const bool rowk_shape = eg.kind == 4 && tokens <= 64 && eg.tile == 4 && eg.ksplit == 2 && eg.unroll == 2 &&
+                          (eg.waves == 4 || eg.waves == 2);
+  bool group = codes && same && (eg.kind == 2 || rowk_shape);
   if (group && ps[0] == 3) {
     if ((st = ensure_scratch(gate, 3)) != UW_OK || (st = ensure_scratch(up, 3)) != UW_OK) return st;
     group = gate->scratch != up->scratch;
@@ -728,7 +732,10 @@ uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, cons
     const uint16_t* xs[2] = {x_dev, x_dev};
     float* ys[2] = {g, u};
     const int64_t ts[2] = {tokens, tokens};
-    UW_HIP(launch_fused_gemv_group(ws, xs, ys, ts, 2, eg, gate->main));
+    if (eg.kind == 2)
+      UW_HIP(launch_fused_gemv_group(ws, xs, ys, ts, 2, eg, gate->main));
+    else
+      UW_HIP(launch_fused_rowk_group(ws, xs, ys, 2, tokens, eg, gate->main));
     if (p3 && ((st = mark_consumed(gate)) != UW_OK || (st = mark_consumed(up)) != UW_OK)) return st;
   } else {
     if ((st = matmul_impl(gate, x_dev, g, tokens, pipelines[0])) != UW_OK) return st;
@@ -1207,7 +1214,7 @@ uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t*
   }
   const int64_t rows = experts[0]->rows, cols = experts[0]->cols;
   // Experts whose call resolves to pipeline 4 with few enough tokens for the
-  // gemv kernels go out together, up to kGemvGroupMax per launch, on the
+  // gemv kernels go out together, up to kFusedGroupMax per launch, on the
   // stream of the first of them: those whose variant is a gemv one, and those
   // left to the default when the group's brick-rows fill the chip (a single
   // short matrix takes the K-split small kernel by default; a group of them
@@ -1233,10 +1240,10 @@ uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t*
     c.cand = c.ev.kind == 2 || (c.var == 0 && fits);
     if (c.cand) cand_brows += brows;
   }
-  uw::FusedW gw[uw::kGemvGroupMax];
-  const uint16_t* gx[uw::kGemvGroupMax];
-  float* gy[uw::kGemvGroupMax];
-  int64_t gt[uw::kGemvGroupMax];
+  uw::FusedW gw[uw::kFusedGroupMax];
+  const uint16_t* gx[uw::kFusedGroupMax];
+  float* gy[uw::kFusedGroupMax];
+  int64_t gt[uw::kFusedGroupMax];
   int ng = 0;
   bool have_group = false;
   uw::Variant gv{};
@@ -1272,7 +1279,7 @@ uw_status uw_grouped_matmul(const uw_handle* experts, int32_t n, const uint16_t*
     gx[ng] = xe;
     gy[ng] = ye;
     gt[ng] = t;
-    if (++ng == uw::kGemvGroupMax) {
+    if (++ng == uw::kFusedGroupMax) {
       uw_status st = flush();
       if (st != UW_OK) return st;
     }

@@ -365,10 +365,11 @@ def test_mlp_layer_8b_shapes(env, pipes):
 
 @pytest.mark.parametrize("gu", [4, 3])
 def test_mlp_forward_gate_up_one_launch(env, gu):
-    """gate and up take the same gemv variant (on the palette form, pipeline
-    4, or on codes decoded into scratch, pipeline 3), so uw_mlp_forward sends
-    them out as one launch: the layer must equal, bit for bit, the same layer
-    run as separate calls (gate, up, silu*mul, down), and the fp64 layer."""
+    """gate and up take the same gemv or whole-K variant (on the palette
+    form, pipeline 4, or on codes decoded into scratch, pipeline 3), so
+    uw_mlp_forward sends them out as one launch: the layer must equal, bit for
+    bit, the same layer run as separate calls (gate, up, silu*mul, down), and
+    the fp64 layer."""
     torch, uw = env
     hidden, inter = 1024, 2048  # 128 brick-rows: the gemv kernels are the default
     ws = [synth.weights(inter, hidden, 60, 0.002, 10), synth.weights(inter, hidden, 61, 0.002, 10),
@@ -377,10 +378,11 @@ def test_mlp_forward_gate_up_one_launch(env, gu):
     # the down projection (64 brick-rows) would split K with atomic sums by
     # default; variant 1 does not, so both runs add in one order
     mats[2].set_variant(1)
-    work = torch.empty(uw.mlp_workspace_bytes(16, inter), dtype=torch.uint8, device="cuda")
-    for tokens in (1, 5, 16):
-        print(f"gate+up one launch, pipeline {gu}, tokens {tokens}", flush=True)
-        assert mats[0].variant_in_use(tokens, gu)[1].startswith("gemv"), mats[0].variant_in_use(tokens, gu)
+    work = torch.empty(uw.mlp_workspace_bytes(64, inter), dtype=torch.uint8, device="cuda")
+    for tokens in (1, 5, 16, 24, 64):
+        kind = mats[0].variant_in_use(tokens, gu)[1]
+        print(f"gate+up one launch, pipeline {gu}, tokens {tokens}, {kind}", flush=True)
+        assert kind.startswith("gemv" if tokens <= 16 else "rowk:r4p4u2d2"), kind
         x = synth.activations(tokens, hidden, xseed=30 + tokens)
         xd = uw.bf16_tensor(x)
         y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
