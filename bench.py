@@ -204,6 +204,47 @@ def load_traffic():
         return None
 
 
+def decode_bench(torch, uw, base, stream, steps, warmup) -> dict:
+    """The preprocessing kernels alone on the gate (Unweight page, section 六):
+    the Huffman decode to bf16 W (P1), to exponent bytes (P2) and to 4-bit
+    palette codes (P3), and the palette form's full decode (P5), each on
+    rotated handles with scratch of their own.  Algorithmic bytes: what the
+    kernel must read from and write to HBM (the per-workgroup decode tables
+    come from L2 and are not counted)."""
+    import numpy as np
+    inf = base.info()
+    rows, cols = base.rows, base.cols
+    n = rows * cols
+    bricks, chunks = n // 1024, n // 256
+    stream_b = inf["stream_words"] * 4 + chunks * 4
+    algo = {1: stream_b + n + 2 * n, 2: stream_b + n, 3: stream_b + 8 * bricks + n // 2,
+            5: n + n // 2 + 8 * bricks + 64 * inf["raw_groups"] + 2 * n}
+    sbytes = max(inf["scratch_bytes"][p] for p in algo)
+    ncopy = max(2, math.ceil((1 << 30) / (inf["resident_bytes"] + sbytes)))
+    mats = [base.clone() for _ in range(ncopy)]
+    bufs = [torch.empty(sbytes, dtype=torch.uint8, device="cuda") for _ in mats]
+    for m, b in zip(mats, bufs):
+        m.set_streams(stream)
+        m.set_scratch(b)
+    res = {"rows": rows, "cols": cols, "copies_rotated": ncopy}
+    for p in (3, 2, 1, 5):
+        i = [0]
+
+        def fn():
+            mats[i[0] % ncopy].preprocess(p)
+            i[0] += 1
+        ms = time_graph(torch, fn, steps, warmup, stream, use_graph=False)
+        gbps = algo[p] / (ms / 1e3) / 1e9
+        res[f"P{p}"] = {"us": round(ms * 1e3, 2), "algorithmic_bytes": int(algo[p]), "GBps": round(gbps, 1),
+                        "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        log(f"decode P{p}: " + json.dumps(res[f"P{p}"]))
+    for m in mats:
+        m.free()
+    del bufs
+    torch.cuda.empty_cache()
+    return res
+
+
 def sweep(torch, uw, synth, stream, steps, warmup):
     """All five pipelines and the uncompressed hipBLASLt baseline on the
     8B-shaped MLP projections at batch 1..1024 (the other configurations)."""
@@ -218,7 +259,7 @@ def sweep(torch, uw, synth, stream, steps, warmup):
         base.set_streams(stream)
         info = base.info()
         ncopy = max(2, math.ceil((1 << 30) / info["resident_bytes"]))
-        mats = [base] + [base.clone() for _ in range(ncopy - 1)]
+        mats = [base.clone() for _ in range(ncopy)]
         for m in mats:
             m.set_streams(stream)
         from decode_gemm_bf16_amd.tune import share_scratch
@@ -410,7 +451,7 @@ def shapes_bench(torch, uw, synth, stream, steps, warmup, tokens_list=(1, 16, 64
         base = uw.Matrix(w, uw.FMT_PALETTE | uw.FMT_HUFFMAN)
         info = base.info()
         ncopy = max(2, math.ceil((1 << 30) / info["resident_bytes"]))
-        mats = [base] + [base.clone() for _ in range(ncopy - 1)]
+        mats = [base.clone() for _ in range(ncopy)]
         for m in mats:
             m.set_streams(stream)
         nwd = max(2, math.ceil((1 << 30) / (2 * rows * cols)))
@@ -584,6 +625,8 @@ def main() -> int:
                     help="time the headline steps as one HIP graph replay instead of K eager calls")
     ap.add_argument("--no-batches", action="store_true", help="skip the 16-1024 token leg")
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time the preprocessing decoders alone (P1/P2/P3 Huffman, P5 palette) on the gate")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
     ap.add_argument("--moe", action="store_true",
@@ -728,6 +771,8 @@ def main() -> int:
             "frac": b["P4"]["mfma_frac"], "kernel": b["P4_kernel"], "avg_launch_us": b["P4"]["us"],
             "best_compressed_route": best, "best_compressed_frac": b[best]["mfma_frac"],
             "uncompressed_hipblaslt_frac": b["bf16_hipblaslt"]["mfma_frac"]}
+    if args.decode:
+        result["decode"] = decode_bench(torch, uw, base, stream, max(20, min(args.steps, 200)), args.warmup)
     if args.sweep:
         result["sweep"] = sweep(torch, uw, synth, stream, args.steps, args.warmup)
     if args.tune:
