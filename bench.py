@@ -22,8 +22,9 @@ against the 8 TB/s HBM peak.  cpu_baseline = the CPU oracle (numpy) doing the
 same decode + matmul on a bounded sample of the rows.
 
 The line also carries the same gate at 16-1024 tokens ("batches": direct
-palette, palette full decode + library GEMM, uncompressed library GEMM) and
-the batch-1024 figure against the bf16 MFMA peak ("roofline_batch1024").
+palette, palette full decode + library GEMM, uncompressed library GEMM), the
+batch-1024 figure against the bf16 MFMA peak ("roofline_batch1024") and the
+preprocessing decoders alone against the HBM peak ("decode").
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep]
 """
@@ -625,8 +626,10 @@ def main() -> int:
                     help="time the headline steps as one HIP graph replay instead of K eager calls")
     ap.add_argument("--no-batches", action="store_true", help="skip the 16-1024 token leg")
     ap.add_argument("--sweep", action="store_true", help="also time all pipelines on the 8B MLP shapes")
-    ap.add_argument("--decode", action="store_true",
-                    help="also time the preprocessing decoders alone (P1/P2/P3 Huffman, P5 palette) on the gate")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the preprocessing decoders alone (P1/P2/P3 Huffman, P5 palette) on the gate")
+    ap.add_argument("--decode", action="store_true", help="time the decoders alone (the default; accepted for "
+                    "older command lines)")
     ap.add_argument("--tune", action="store_true", help="also run the autotuner on the 8B MLP layer")
     ap.add_argument("--stack", action="store_true", help="also time the 80-layer 70B-shaped stack")
     ap.add_argument("--moe", action="store_true",
@@ -771,7 +774,7 @@ def main() -> int:
             "frac": b["P4"]["mfma_frac"], "kernel": b["P4_kernel"], "avg_launch_us": b["P4"]["us"],
             "best_compressed_route": best, "best_compressed_frac": b[best]["mfma_frac"],
             "uncompressed_hipblaslt_frac": b["bf16_hipblaslt"]["mfma_frac"]}
-    if args.decode:
+    if not args.no_decode:
         result["decode"] = decode_bench(torch, uw, base, stream, max(20, min(args.steps, 200)), args.warmup)
     if args.sweep:
         result["sweep"] = sweep(torch, uw, synth, stream, args.steps, args.warmup)
