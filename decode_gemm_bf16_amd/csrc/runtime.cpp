@@ -117,15 +117,65 @@ uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, i
     uint64_t ws = kBlasWs;
     hipblasLtMatmulPreferenceCreate(&pref);
     hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &ws, sizeof ws);
-    hipblasLtMatmulHeuristicResult_t res[1];
+    constexpr int kCand = 16;
+    hipblasLtMatmulHeuristicResult_t res[kCand];
     int got = 0;
     hipblasStatus_t hs =
-        hipblasLtMatmulAlgoGetHeuristic(g_blas, p.desc, p.a, p.b, p.c, p.c, pref, 1, res, &got);
+        hipblasLtMatmulAlgoGetHeuristic(g_blas, p.desc, p.a, p.b, p.c, p.c, pref, kCand, res, &got);
     hipblasLtMatmulPreferenceDestroy(pref);
     if (hs != HIPBLAS_STATUS_SUCCESS || got < 1)
       return fail(UW_ERR_HIP, "hipBLASLt has no bf16->f32 algorithm for m=%lld n=%lld k=%lld", (long long)m,
                   (long long)n, (long long)k);
     p.algo = res[0].algo;
+    // The library's first-ranked algorithm is not always its fastest (8B
+    // down projection at 1024 tokens, weights read from HBM: 118 against 98
+    // us for the third): on the first call of a shape, time the candidates on
+    // the caller's buffers and keep the fastest.  Each timed call follows a
+    // 512 MiB read that evicts the operands from L2 and the Infinity Cache,
+    // as in use, where the weights stream from HBM (timed on cache-resident
+    // operands the choice is a different, slower one at small batch).  Every
+    // call writes the same y; the real call follows.  Skipped while the
+    // stream is being captured into a graph, or when the eviction buffer
+    // cannot be allocated.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    void* flush = nullptr;
+    constexpr size_t kFlush = size_t(512) << 20;
+    if (got > 1 && hipStreamIsCapturing(s, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone &&
+        hipMalloc(&flush, kFlush + 16) == hipSuccess) {
+      hipEvent_t e0 = nullptr, e1 = nullptr;
+      if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+        const float alpha = 1.f, beta = 0.f;
+        float best = 0.f;
+        for (int i = 0; i < got; ++i) {
+          // warm-up (and a check that the candidate runs)
+          if (hipblasLtMatmul(g_blas, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.c, y, p.c, &res[i].algo,
+                              ws_of_stream, kBlasWs, s) != HIPBLAS_STATUS_SUCCESS)
+            continue;
+          constexpr int kReps = 3;
+          float total = 0.f;
+          bool ok = true;
+          for (int r = 0; r < kReps && ok; ++r) {
+            float ms = 0.f;
+            ok = uw::launch_read(flush, static_cast<uint8_t*>(flush) + kFlush, kFlush, s) == hipSuccess &&
+                 hipEventRecord(e0, s) == hipSuccess &&
+                 hipblasLtMatmul(g_blas, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.c, y, p.c, &res[i].algo,
+                                 ws_of_stream, kBlasWs, s) == HIPBLAS_STATUS_SUCCESS &&
+                 hipEventRecord(e1, s) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+                 hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+            total += ms;
+          }
+          if (!ok) break;
+          if (i == 0 || total < best) {
+            best = total;
+            p.algo = res[i].algo;
+          }
+        }
+      }
+      if (e0) (void)hipEventDestroy(e0);
+      if (e1) (void)hipEventDestroy(e1);
+      (void)hipStreamSynchronize(s);
+      (void)hipFree(flush);
+    }
     it = g_plans.emplace(key, p).first;
   }
   const float alpha = 1.f, beta = 0.f;

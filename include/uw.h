@@ -327,7 +327,11 @@ int32_t uw_device_cu_count(void);
 /* ---- Reference points for measurement ---- */
 
 /* Uncompressed baseline: y[tokens, rows] = x * w^T with w_dev a plain bf16
- * [rows, cols] matrix, through hipBLASLt (the library GEMM of pipeline 1). */
+ * [rows, cols] matrix, through hipBLASLt (the library GEMM of pipelines 1 and
+ * 5).  The first call of a (tokens, rows, cols) shape, unless the stream is
+ * being captured into a graph, times up to 16 of the library's candidate
+ * algorithms on the given buffers and keeps the fastest for that shape (the
+ * host waits for it, once); later calls only enqueue. */
 uw_status uw_gemm_bf16(const uint16_t* x_dev, const uint16_t* w_dev, float* y_dev, int64_t tokens,
                        int64_t rows, int64_t cols, void* stream);
 
