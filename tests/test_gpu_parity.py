@@ -401,6 +401,40 @@ def test_mlp_forward_gate_up_one_launch(env, gu):
         assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL, tokens
 
 
+def test_mlp_forward_shared_scratch_pipeline3(env):
+    """gate and up decoded into one shared scratch buffer (pipeline 3): the
+    layer must not send their products out as one launch (up's decode would
+    overwrite gate's codes first); it runs them one after the other and still
+    matches the fp64 layer and the separate calls bit for bit."""
+    torch, uw = env
+    hidden, inter, tokens = 1024, 2048, 1
+    ws = [synth.weights(inter, hidden, 80, 0.002, 10), synth.weights(inter, hidden, 81, 0.002, 10),
+          synth.weights(hidden, inter, 82, 0.002, 10)]
+    mats = [_both(env, w) for w in ws]
+    mats[2].set_variant(1)  # no K split in the down projection: one summation order
+    shared = torch.empty(mats[0].info()["scratch_bytes"][3], dtype=torch.uint8, device="cuda")
+    mats[0].set_scratch(shared)
+    mats[1].set_scratch(shared)
+    x = synth.activations(tokens, hidden, xseed=40)
+    xd = uw.bf16_tensor(x)
+    work = torch.empty(uw.mlp_workspace_bytes(tokens, inter), dtype=torch.uint8, device="cuda")
+    y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+    print("shared scratch, pipeline 3 gate/up", flush=True)
+    uw.mlp_forward(*mats, [3, 3, 4], xd, y, tokens, work)
+    g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
+    u = torch.empty_like(g)
+    h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
+    y2 = torch.empty_like(y)
+    mats[0].matmul(xd, g, tokens, 3)
+    mats[1].matmul(xd, u, tokens, 3)
+    uw.silu_mul(g, u, h)
+    mats[2].matmul(h, y2, tokens, 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), y2.cpu().numpy())
+    _, _, _, ref = oracle.mlp_layer_fp64(x, *ws)
+    assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL
+
+
 def test_silu_mul(env):
     torch, uw = env
     rng = np.random.default_rng(4)
