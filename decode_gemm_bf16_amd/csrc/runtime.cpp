@@ -758,6 +758,16 @@ uw_status mlp_forward_impl(uw_matrix* gate, uw_matrix* up, uw_matrix* down, cons
   float* u = carve<float>(cur, size_t(tokens) * inter * 4);
   uint16_t* hh = carve<uint16_t>(cur, size_t(tokens) * inter * 2);
   uw_status st;
+  // up's and down's preprocessing (Huffman or palette decode into their
+  // scratch) goes to their side streams first, where they have one, so that
+  // it runs while gate's product does (the page's side-stream decode, within
+  // the layer); their products wait for it
+  for (int j = 1; j < 3; ++j) {
+    const int p = ps[j];
+    if ((p == 1 || p == 2 || p == 3 || p == 5) && hs[j]->side != hs[j]->main && hs[j]->prep_pipeline != p &&
+        (st = uw_preprocess(hs[j], p)) != UW_OK)
+      return st;
+  }
   // gate and up read the same activations: when both run the same gemv or
   // whole-K variant on 4-bit codes -- the palette form (pipeline 4) or codes
   // decoded into scratch (pipeline 3, separate scratch buffers) -- they go out

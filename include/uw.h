@@ -283,7 +283,10 @@ uw_status uw_silu_mul(const float* g_dev, const float* u_dev, uint16_t* h_dev, i
  * memory for the gate/up outputs and h.  Runs on gate's main stream.  When
  * gate and up resolve to the same gemv variant on 4-bit codes (pipeline 4, or
  * pipeline 3 with separate scratch buffers), their products go out as one
- * kernel launch; the results are those of two uw_matmul calls. */
+ * kernel launch; the results are those of two uw_matmul calls.  up's and
+ * down's preprocessing (pipelines 1-3 and 5) is issued first on their side
+ * streams where uw_set_streams gave them one, so that it overlaps gate's
+ * product (as uw_preprocess would; their products wait for it). */
 uw_status uw_mlp_forward(uw_handle gate, uw_handle up, uw_handle down, const int32_t* pipelines,
                          const uint16_t* x_dev, float* y_dev, int64_t tokens, void* work_dev,
                          size_t work_bytes);

@@ -435,6 +435,35 @@ def test_mlp_forward_shared_scratch_pipeline3(env):
     assert oracle.rel_err(y.cpu().numpy(), ref) <= TOL
 
 
+@pytest.mark.parametrize("pipes", [[5, 5, 5], [3, 3, 3], [1, 2, 3]])
+def test_mlp_forward_side_stream_decodes(env, pipes):
+    """With a side stream on the handles, uw_mlp_forward decodes up and down
+    there while gate's product runs: the layer must equal, bit for bit, the
+    same layer on one stream, and the fp64 layer."""
+    torch, uw = env
+    hidden, inter, tokens = 1024, 2048, 7
+    ws = [synth.weights(inter, hidden, 90, 0.002, 10), synth.weights(inter, hidden, 91, 0.002, 10),
+          synth.weights(hidden, inter, 92, 0.002, 10)]
+    mats = [_both(env, w) for w in ws]
+    mats[2].set_variant(1)  # no K split in the down projection: one summation order
+    x = synth.activations(tokens, hidden, xseed=50)
+    xd = uw.bf16_tensor(x)
+    work = torch.empty(uw.mlp_workspace_bytes(tokens, inter), dtype=torch.uint8, device="cuda")
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    outs = []
+    for s2 in (main, side):
+        for m in mats:
+            m.set_streams(main, s2)
+        y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        print(f"layer {pipes}, side stream {s2 is side}", flush=True)
+        uw.mlp_forward(*mats, pipes, xd, y, tokens, work)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+    _, _, _, ref = oracle.mlp_layer_fp64(x, *ws)
+    assert oracle.rel_err(outs[1], ref) <= TOL
+
+
 def test_silu_mul(env):
     torch, uw = env
     rng = np.random.default_rng(4)
