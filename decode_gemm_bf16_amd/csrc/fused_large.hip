@@ -846,9 +846,11 @@ hipError_t launch_large_il(const FusedW& w, const uint16_t* x, float* y, int64_t
 // 10 = tile 8 with the next step's rebuild interleaved into the MFMAs; 11 = 10 with B fragments
 // read in groups of 8, one group ahead; 12-14: deep-prefetch tiles of fused_ring.hip
 hipError_t launch_fused_ring(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, int tile, hipStream_t s);
+hipError_t launch_fused_wide(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, hipStream_t s);
 
 hipError_t launch_fused_large(const FusedW& w, const uint16_t* x, float* y, int64_t tokens, const Variant& v,
                               hipStream_t s) {
+  if (v.tile == 22) return launch_fused_wide(w, x, y, tokens, s);  // no K split
   if (v.tile >= 12) return launch_fused_ring(w, x, y, tokens, v.tile, s);  // no K split
   const int ks = v.ksplit < 1 ? 1 : v.ksplit;
   if (ks > 1) {

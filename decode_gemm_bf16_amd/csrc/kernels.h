@@ -48,6 +48,9 @@ constexpr int64_t kGemvXElems = 16384;
 // Whether a rowk variant's LDS fits for this shape (else it cannot launch).
 bool rowk_fits(int64_t tokens, int64_t rows, int64_t cols, const Variant& v);
 constexpr int64_t kGemvKbnMax = 1024;
+// Longest K (in 64-column bricks) of the wide large-batch tile (tile 22),
+// whose LDS holds its 8 brick-rows' tables.
+constexpr int64_t kWideKbnMax = 256;
 // LDS budget of the mid kernels (a K slice of the activations plus the
 // per-brick tables, or the epilogue's partial sums): two workgroups per CU.
 constexpr size_t kMidLdsBytes = 81920;

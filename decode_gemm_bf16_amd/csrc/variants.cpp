@@ -80,6 +80,8 @@ const Named kLarge[] = {
     {{1, 0, 1, 0, 19}, "large:t19(4x32r x64t,32x32,ring d4 x8 b3)"},
     {{1, 0, 1, 0, 20}, "large:t20(4x32r x128t,32x32,ring d4 x8 b4)"},
     {{1, 0, 1, 0, 21}, "large:t21(4x64r x128t,32x32,ring d2 x3 b2)"},
+    // 128 rows rebuilt once per 512 tokens into LDS, shared by 4 waves of 128 tokens
+    {{1, 0, 1, 0, 22}, "large:t22(128r x 4x128t,32x32,wide)"},
     // whole K per workgroup, 16x16x32 instructions, up to 128 tokens
     {{4, 4, 1, 2, 4}, "rowk:r4p4u1d2"},   {{4, 2, 2, 2, 4}, "rowk:r4p2u2d2"},
     {{4, 2, 1, 2, 4}, "rowk:r4p2u1d2"},   // up to 256 tokens
@@ -176,6 +178,11 @@ Variant variant_default(int64_t tokens, int64_t rows, int64_t cols) {
   // per brick-row, activations streamed through LDS in 4-brick slices)
   const Variant rowk{4, 2, 2, 2, 4};
   if (tokens <= 128 && rowk_fits(tokens, rows, cols, rowk)) return rowk;
+  // from 768 tokens: 128-row x 512-token workgroups that rebuild each weight
+  // once for their 512 tokens into LDS, where they fill most of the chip and
+  // the brick tables fit their LDS
+  const int64_t wg22 = ((brows + 7) / 8) * ((tokens + 511) / 512);
+  if (tokens >= 768 && kbn <= kWideKbnMax && wg22 >= 192) return Variant{1, 0, 1, 0, 22};
   // 256 x 256 tiles with the rebuild interleaved into the MFMAs once there are
   // enough tokens to fill the chip with them (one workgroup per CU)
   const int64_t wg11 = ((brows + 15) / 16) * ((tokens + 255) / 256);
@@ -218,6 +225,8 @@ Variant variant_effective(int64_t tokens, int64_t rows, int64_t cols, bool exp_m
   if (tokens <= 64 && v.kind == 2 &&
       !(!exp_mode && tokens <= 16 && tokens * cols <= kGemvXElems && cols / 64 <= kGemvKbnMax))
     v = small_default(tokens, rows, cols);
+  // the wide tile keeps the brick tables of its 8 brick-rows in LDS
+  if (v.kind == 1 && v.tile == 22 && cols / 64 > kWideKbnMax) v = variant_default(tokens, rows, cols);
   // a whole-K shape whose slices and tables do not fit LDS (or more tokens
   // than it is built for): the K-slice kernel, or the large-batch default
   if (v.kind == 4 && !rowk_fits(tokens, rows, cols, v))

@@ -157,12 +157,34 @@ def test_ragged_k_slices_and_ring_tails(env, tokens):
     m = _both(env, w)
     names = uw.variants(tokens)
     picked = [v for v, n in enumerate(names)
-              if n.startswith(("mid", "rowk", "large:t1", "small:default", "large:default"))]
+              if n.startswith(("mid", "rowk", "large:t1", "large:t22", "small:default", "large:default"))]
     assert picked
     for v in picked:
         for p in (2, 4):
             y = _run(env, m, x, p, variant=v)
             assert oracle.rel_err(y, ref) <= TOL, (names[v], p, oracle.rel_err(y, ref))
+
+
+@pytest.mark.parametrize("tokens", [513, 700, 1024])
+def test_wide_tile_partial_blocks(env, tokens):
+    """The 128-row x 512-token tile (weights rebuilt into LDS once per 512
+    tokens) on 34 brick-rows (the last row block has 2 of 8), 27 bricks along
+    K (an odd count: the loop runs one brick column past the end) and a last
+    token block that is partly or wholly empty; exponent form (pipeline 2),
+    runtime transcode (3) and direct palette (4) against fp64."""
+    torch, uw = env
+    w = synth.weights(544, 1728, 5, 0.003, 11)
+    x = synth.activations(tokens, 1728, xseed=11)
+    ref = oracle.matmul_fp64(x, w)
+    m = _both(env, w)
+    names = uw.variants(tokens)
+    v = next(i for i, n in enumerate(names) if n.startswith("large:t22"))
+    for p in (2, 3, 4):
+        y = _run(env, m, x, p, variant=v)
+        assert oracle.rel_err(y, ref) <= TOL, (p, oracle.rel_err(y, ref))
+        for br in range(w.shape[0] // 16):
+            sl = slice(16 * br, 16 * br + 16)
+            assert oracle.rel_err(y[:, sl], ref[:, sl]) <= TOL, (p, br)
 
 
 @pytest.mark.parametrize("tokens", [5, 17, 64])
