@@ -344,18 +344,19 @@ def test_mlp_8b_shapes_every_row(env, proj):
 @pytest.mark.parametrize("rows,cols", [(28672, 8192), (8192, 28672)])
 def test_70b_shapes_every_row(env, rows, cols):
     """70B-shaped gate/up (28672 x 8192) and down (8192 x 28672) projections at
-    1 and 256 tokens -- the shapes and batches the layer stack runs: the direct
-    palette and the hard layers' pipelines (runtime transcode, full decode)
-    with the built-in kernel choice (at 256 tokens the down projection runs the
-    whole-K kernel over 448 bricks), every output element against fp64."""
+    1, 256 and 1024 tokens -- the shapes and batches the layer stack runs: the
+    direct palette and the hard layers' pipelines (runtime transcode, full
+    decode) with the built-in kernel choice (at 256 tokens the down projection
+    runs the whole-K kernel over 448 bricks; at 1024 the gate runs the wide
+    tile in two rounds of 224 workgroups), every output element against fp64."""
     torch, uw = env
     c = synth.CONFIGS["stack_70b"]
     w = synth.weights(rows, cols, c["seed_base"] + (2 if rows < cols else 0), c["p"], c["shift"])
     m = _both(env, w)
     wt = oracle.bf16_to_f64(w).T.copy()
     del w
-    xs = synth.activations(256, cols, xseed=1)
-    for tokens in (1, 256):
+    xs = synth.activations(1024, cols, xseed=1)
+    for tokens in (1, 256, 1024):
         x = xs[:tokens]
         ref = oracle.bf16_to_f64(x) @ wt
         for p in (4, 3, 1):

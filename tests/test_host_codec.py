@@ -169,6 +169,27 @@ def test_variant_in_use_resolution():
     assert e.value.status in (uw.ERR_UNSUPPORTED, uw.ERR_INVALID_ARG)
 
 
+def test_wide_tile_choice():
+    """The 128-row x 512-token tile is the built-in choice from 768 tokens
+    where its workgroups fill at least 192 CUs; its brick tables live in LDS,
+    so for K beyond 256 bricks an explicit request falls back to the
+    built-in choice of the shape (no GPU work)."""
+    tall = uw.Matrix(synth.weights(14336, 1024, 1, 0.0005, 10), HOST_ALL)  # 112 row blocks of 128
+    assert tall.variant_in_use(1024)[1].startswith("large:t22")
+    assert tall.variant_in_use(768)[1].startswith("large:t22")
+    assert not tall.variant_in_use(512)[1].startswith("large:t22")  # 112 workgroups: half the chip
+    tall.free()
+    short = uw.Matrix(synth.weights(4096, 1024, 1, 0.0005, 10), HOST_ALL)  # 32 row blocks
+    assert not short.variant_in_use(1024)[1].startswith("large:t22")
+    short.free()
+    longk = uw.Matrix(synth.weights(64, 257 * 64, 1, 0.0005, 10), HOST_ALL)  # K of 257 bricks
+    v = uw.variants(1024).index("large:t22(128r x 4x128t,32x32,wide)")
+    longk.set_variant(v)
+    assert longk.variant_in_use(1024) == (uw.P4_DIRECT_PALETTE, longk.variant_in_use(1024, uw.P4_DIRECT_PALETTE)[1])
+    assert not longk.variant_in_use(1024)[1].startswith("large:t22")
+    longk.free()
+
+
 def test_bits_per_weight_on_gate_shaped_slice():
     """North-star size target: >= 20% fewer weight bytes than bf16 in both forms."""
     w = synth.weights(1024, 4096, 0, 0.0005, 10)
