@@ -23,10 +23,12 @@
 // LDS), palette codes through a 64-bit register queue whose low dword is
 // stored, aligned, after every lookup.  A run (16 symbols) is emitted once
 // both chains of every lane of the wave hold one; a chain may run up to half
-// a run ahead.  The table and the workgroup's bits are first moved into LDS
-// by buffer loads straight to LDS (a workgroup whose span does not fit, which
-// needs more than 2.8 bits per exponent on average -- 3.3 for pipeline 3 --
-// reads its words from global memory).  The grid gives every workgroup the
+// a run ahead (palette codes: a whole run, which spares the wave 7% of its
+// lookup steps -- it waits less often for its slowest chain).  The table and
+// the workgroup's bits are first moved into LDS by buffer loads straight to
+// LDS (a workgroup whose span does not fit, which needs more than 2.8 bits
+// per exponent on average -- 3.1 for pipeline 3 -- reads its words from
+// global memory).  The grid gives every workgroup the
 // same number of chunks (at most 512), chosen so that the workgroups fill
 // whole rounds of two per CU: on the 14336 x 4096 gate 512 workgroups of 448
 // chunks instead of 448 of 512, which left a quarter of the CUs with one
@@ -50,14 +52,14 @@ constexpr int kChunksPerBlock = 2 * kThreads;   // the interleave group of the s
 constexpr int kStreamPad = 8;                   // zero words after the stream (the encoder's padding)
 constexpr int kSymSlot = 36;                    // bytes per chunk (9 dwords: the lanes' slots start in distinct banks)
 constexpr uint32_t kSymLead = 24;               // a pair of lookups is taken while a slot holds fewer symbols
-constexpr int kCodeSlot = 5;                    // dwords per chunk for palette codes
-constexpr uint32_t kCodeLead = 3;               // a pair is taken while fewer dwords are full
+constexpr int kCodeSlot = 6;                    // dwords per chunk for palette codes
+constexpr uint32_t kCodeLead = 4;               // a pair is taken while fewer dwords are full
 
 // Staged bitstream, in words: LDS per workgroup = 16 KB table + stage + slots,
 // two workgroups per CU.
 template <int EMIT>
 constexpr int stage_words() {
-  return EMIT == EMIT_NIBBLE ? 13568 : 11520;
+  return EMIT == EMIT_NIBBLE ? 13056 : 11520;
 }
 
 // Exponent bytes and palette codes are written once and read by a later
@@ -267,12 +269,15 @@ __device__ __forceinline__ void decode_codes(Src src, uint32_t base, int64_t ca,
       refill(src, bb);
       if (!__any(qa.kb < 8u || qb.kb < 8u)) break;
     }
-    const uint32_t a0 = slot_a[0], a1 = slot_a[1], a2 = slot_a[2], a3 = slot_a[3];
-    const uint32_t b0 = slot_b[0], b1 = slot_b[1], b2 = slot_b[2], b3 = slot_b[3];
+    // (up to 5 full dwords: the run's 2 leave, the other 3 move down)
+    const uint32_t a0 = slot_a[0], a1 = slot_a[1], a2 = slot_a[2], a3 = slot_a[3], a4 = slot_a[4];
+    const uint32_t b0 = slot_b[0], b1 = slot_b[1], b2 = slot_b[2], b3 = slot_b[3], b4 = slot_b[4];
     slot_a[0] = a2;
     slot_a[1] = a3;
+    slot_a[2] = a4;
     slot_b[0] = b2;
     slot_b[1] = b3;
+    slot_b[2] = b4;
     qa.kb -= 8u;
     qb.kb -= 8u;
     st8(rs_out, stored_codes(a0, a1, (rawa >> run) & 1u), va, (uint32_t)run * (8u * kChunksPerBlock));
