@@ -299,7 +299,7 @@ std::vector<uint32_t> multi_code_table(const std::vector<uint16_t>& lut, const u
       ++cnt;
       pos += len;
     }
-    out[p] = codes | ((4 * cnt) << 22) | (pos << 27);
+    out[p] = codes | (pos << 20) | ((4 * cnt) << 24);
   }
   return out;
 }

@@ -68,8 +68,8 @@ std::vector<uint32_t> multi_symbol_table(const std::vector<uint16_t>& lut);
 // Decode table for pipeline 3: for each 12-bit window, the 4-bit palette
 // codes (code_of[symbol]; symbols outside the palette, which only occur in
 // raw groups, get 0) of the whole codes it starts with, greedily and at most
-// five: bits 0-19 the codes (first in the low nibble), bits 22-26 four times
-// their count (the bits they fill), bits 27-31 the bits they take.
+// five: bits 0-19 the codes (first in the low nibble), bits 20-23 the bits
+// they take, bits 24-31 four times their count (the bits they fill).
 std::vector<uint32_t> multi_code_table(const std::vector<uint16_t>& lut, const uint8_t code_of[256]);
 
 // Section 四: the palette of a histogram (the 16 most frequent exponents, ties

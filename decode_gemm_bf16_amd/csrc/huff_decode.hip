@@ -136,8 +136,9 @@ __device__ __forceinline__ u32x4 take_sym_run(uint8_t* slot, uint32_t& p) {
   return e;
 }
 
-// Palette codes: an entry holds up to five codes (bits 0-19), four times
-// their count (22-26) and the bits they take (27-31).  The codes not yet
+// Palette codes: an entry holds up to five codes (bits 0-19), the bits they
+// take (20-23) and four times their count (the top byte, which an add reads
+// through a byte select: no separate extract).  The codes not yet
 // completing a dword wait in q (qs bits of it); a lookup shifts its codes by
 // qs as one 64-bit value, stores q with their low part at byte kb of the slot,
 // and when the dword is full moves on to the next one, keeping the high part.
@@ -148,11 +149,11 @@ struct CodeQ {
 __device__ __forceinline__ void lookup_code(BitBuf& bb, CodeQ& cq, bool take, uint8_t* slot, const uint8_t* lut) {
   uint32_t ent = table_entry(bb, lut);
   ent = take ? ent : 0u;
-  bb.r -= (int32_t)(ent >> 27);
+  bb.r -= (int32_t)((ent >> 20) & 15u);
   const uint64_t c = (uint64_t)(ent & 0xFFFFFu) << cq.qs;
   const uint32_t lo = cq.q | (uint32_t)c;
   *(uint32_t*)(slot + cq.kb) = lo;
-  const uint32_t sum = cq.qs + ((ent >> 22) & 31u);
+  const uint32_t sum = cq.qs + (ent >> 24);
   const bool mv = sum >= 32u;
   cq.q = mv ? (uint32_t)(c >> 32) : lo;
   cq.qs = sum & 31u;
