@@ -405,6 +405,7 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
     out = {"layers": L, "resident_GB": round(resident / 1e9, 2), "distinct_layers_generated": 4,
            "hard": "even layers, Huffman + runtime palette transcode (P3)", "easy": "odd layers, direct palette (P4)"}
     xs = synth.activations(max(tokens_list), hidden, xseed=1)
+    easy = None  # the same stack with every layer easy, built on first use
     for tokens in tokens_list:
         x = uw.bf16_tensor(xs[:tokens])
         # side-stream CU counts; all CUs = both streams share every CU
@@ -412,15 +413,29 @@ def stack_bench(torch, uw, synth, tokens_list, steps: int):
                          steps=steps, log=log)
         best_ms, best_split = res[0]
         serial = [ms for ms, n in res if n == 0][0]
+        easy_ms = None
+        if tokens <= 64:
+            # every layer in the direct-palette form (the hard layers' weights
+            # encoded again as palette): 80 x 3 projections through P4
+            if easy is None:
+                pal = [distinct[l] if l % 2 else
+                       [uw.Matrix(synth.weights(sh[0], sh[1], c["seed_base"] + 3 * l + j, c["p"], c["shift"]),
+                                  uw.FMT_PALETTE) for j, sh in enumerate((c["gate"], c["up"], c["down"]))]
+                       for l in range(4)]
+                easy = [pal[l % 4][j] if l < 4 else pal[l % 4][j].clone() for l in range(L) for j in range(3)]
+            easy_ms = tune_split(torch, easy, [4] * len(easy), x, tokens, [0], steps=steps, log=log)[0][0]
         # all layers read as direct palette would need palette copies of the hard layers; time instead the
         # uncompressed bf16 stack: 4 distinct bf16 layers cycled (each 1.4 GB, no cache reuse across layers)
         bms = bf16_stack_ms(torch, uw, synth, c, x, tokens)
         out[str(tokens)] = {"serial_us": round(serial * 1e3, 1), "overlap_best_us": round(best_ms * 1e3, 1),
                             "best_side_cus": best_split, "splits": {str(n): round(ms * 1e3, 1) for ms, n in res},
                             "bf16_hipblaslt_us": round(bms * 1e3, 1),
+                            "all_easy_p4_serial_us": None if easy_ms is None else round(easy_ms * 1e3, 1),
                             "weight_GB_per_pass_bf16": round(2 * 3 * L * hidden * inter / 1e9, 1)}
         log("stack", tokens, json.dumps(out[str(tokens)]))
     for m in stack:
+        m.free()
+    for m in easy or []:
         m.free()
     return out
 
