@@ -27,7 +27,8 @@ import sys
 import time
 
 from . import (FMT_HUFFMAN, FMT_PALETTE, Matrix, mlp_forward, mlp_workspace_bytes, variants,
-               stack_forward, stack_workspace_bytes, stream_create, stream_destroy, device_cu_count, bf16_tensor)
+               stack_forward, stack_workspace_bytes, stream_create, stream_destroy, device_cu_count, bf16_tensor,
+               gemm_bf16, silu_mul)
 
 PROJECTIONS = ("gate", "up", "down")
 
@@ -278,6 +279,56 @@ def tune_split(torch, stack: list[Matrix], pipes: list[int], x, tokens: int, spl
     return out
 
 
+def layer_baselines(torch, layer: dict, weights: dict, tokens_list, stream, steps: int = 10) -> dict:
+    """Layer times (us) next to a tuned plan: the built-in choice on the
+    palette form (pipeline 4 for all three projections, variant 0) and the
+    uncompressed layer (hipBLASLt gate, up and down on bf16 copies, silu*mul
+    between), both on rotated copies."""
+    gate0 = layer["gate"][0]
+    inter, hidden = gate0.rows, gate0.cols
+    ncopy = min(len(layer[p]) for p in PROJECTIONS)
+    nbf = max(2, math.ceil((1 << 30) / (2 * 3 * inter * hidden)))
+    wd = [{p: bf16_tensor(weights[p]) for p in PROJECTIONS} for _ in range(nbf)]
+    out = {}
+    for tokens in tokens_list:
+        x = torch.randn(tokens, hidden, device="cuda").to(torch.bfloat16)
+        y = torch.empty((tokens, hidden), device="cuda", dtype=torch.float32)
+        work = torch.empty(mlp_workspace_bytes(tokens, inter), dtype=torch.uint8, device="cuda")
+        i = [0]
+
+        def fused():
+            k = i[0] % ncopy
+            mlp_forward(layer["gate"][k], layer["up"][k], layer["down"][k], [4, 4, 4], x, y, tokens, work)
+            i[0] += 1
+        g = torch.empty((tokens, inter), device="cuda", dtype=torch.float32)
+        u = torch.empty_like(g)
+        h = torch.empty((tokens, inter), device="cuda", dtype=torch.int16)
+        j = [0]
+
+        def plain():
+            w = wd[j[0] % nbf]
+            gemm_bf16(x, w["gate"], g, tokens, inter, hidden, stream)
+            gemm_bf16(x, w["up"], u, tokens, inter, hidden, stream)
+            silu_mul(g, u, h, stream)
+            gemm_bf16(h, w["down"], y, tokens, hidden, inter, stream)
+            j[0] += 1
+        plain()  # the library's candidate timing of each shape, once
+        torch.cuda.synchronize()
+        out[str(tokens)] = {"builtin_P4_us": round(time_graph(torch, fused, steps, 2, stream) * 1e3, 2),
+                            "bf16_hipblaslt_us": round(time_graph(torch, plain, steps, 2, stream) * 1e3, 2)}
+    del wd
+    return out
+
+
+# hidden and intermediate sizes of the SwiGLU layers tuned by main(), by model family
+MODEL_SHAPES = {
+    "8b": (4096, 14336, "Llama-3.1-8B"),
+    "qwen7b": (3584, 18944, "Qwen2.5-7B"),
+    "nemo12b": (5120, 14336, "Mistral-NeMo-12B"),
+    "llama3b": (3072, 8192, "Llama-3.2-3B"),
+}
+
+
 def main(argv=None) -> int:
     import argparse
     import os
@@ -286,18 +337,27 @@ def main(argv=None) -> int:
     sys.path.insert(0, root)
     import synth
 
-    ap = argparse.ArgumentParser(description="tune pipelines and kernel variants of an 8B-shaped MLP layer")
+    ap = argparse.ArgumentParser(description="tune pipelines and kernel variants of a SwiGLU MLP layer")
     ap.add_argument("--batches", default="1,16,64,256,1024")
+    ap.add_argument("--model", default="8b", choices=sorted(MODEL_SHAPES),
+                    help="layer shape: hidden x intermediate of a model family (synthetic weights)")
+    ap.add_argument("--baselines", action="store_true",
+                    help="also time the built-in choice and the uncompressed hipBLASLt layer")
     ap.add_argument("--out", default="")
     ap.add_argument("--keep", type=int, default=3)
     args = ap.parse_args(argv)
     torch.cuda.set_device(0)
     c = synth.CONFIGS["mlp_8b"]
+    hidden, inter, label = MODEL_SHAPES[args.model]
+    shapes = {"gate": (inter, hidden), "up": (inter, hidden), "down": (hidden, inter)}
     stream = torch.cuda.Stream()
     layer = {}
+    weights = {}
     for proj in PROJECTIONS:
-        rows, cols, seed = c[proj]
-        m = Matrix(synth.weights(rows, cols, seed, c["p"], c["shift"]), FMT_HUFFMAN | FMT_PALETTE)
+        rows, cols = shapes[proj]
+        seed = c[proj][2] if args.model == "8b" else 200 + PROJECTIONS.index(proj)
+        weights[proj] = synth.weights(rows, cols, seed, c["p"], c["shift"])
+        m = Matrix(weights[proj], FMT_HUFFMAN | FMT_PALETTE)
         m.set_streams(stream)
         layer[proj] = copies_for(m, 1 << 30)
         for mm in layer[proj]:
@@ -307,7 +367,12 @@ def main(argv=None) -> int:
         layer[proj] = layer[proj][:n]
     plan = tune_mlp(torch, layer, [int(t) for t in args.batches.split(",")], stream, keep=args.keep,
                     log=lambda s: print(s, file=sys.stderr, flush=True))
-    plan["model"] = "8B-shaped SwiGLU MLP (gate/up 14336x4096, down 4096x14336), synthetic weights"
+    if args.baselines:
+        plan["baselines"] = layer_baselines(torch, layer, weights, [int(t) for t in args.batches.split(",")],
+                                            stream)
+        print(f"baselines: {json.dumps(plan['baselines'])}", file=sys.stderr, flush=True)
+    plan["model"] = (f"{label}-shaped SwiGLU MLP (gate/up {inter}x{hidden}, down {hidden}x{inter}), "
+                     "synthetic weights")
     plan["device"] = torch.cuda.get_device_name(0)
     text = json.dumps(plan, indent=1)
     if args.out:

@@ -365,6 +365,34 @@ def test_70b_shapes_every_row(env, rows, cols):
             assert oracle.rel_err(y, ref) <= TOL, (tokens, p, oracle.rel_err(y, ref))
 
 
+# the other SwiGLU projection shapes the bench sweeps (seed 100 + index, as there)
+OTHER_SWIGLU = [(0, 18944, 3584), (1, 3584, 18944), (2, 14336, 5120), (3, 5120, 14336), (4, 8192, 3072),
+                (5, 3072, 8192)]
+
+
+@pytest.mark.parametrize("idx,rows,cols", OTHER_SWIGLU)
+def test_other_swiglu_shapes_every_row(env, idx, rows, cols):
+    """Qwen2.5-7B-, Mistral-NeMo-12B- and Llama-3.2-3B-sized gate/up and down
+    projections (synthetic weights of the 8B recipe) at 1-1024 tokens with the
+    built-in kernel choice: direct palette and runtime transcode at every
+    batch, full decode, exponent decode and the palette full decode at 1 and
+    256 tokens; every output element against fp64."""
+    torch, uw = env
+    c = synth.CONFIGS["mlp_8b"]
+    w = synth.weights(rows, cols, 100 + idx, c["p"], c["shift"])
+    m = _both(env, w)
+    wt = oracle.bf16_to_f64(w).T.copy()
+    del w
+    xs = synth.activations(1024, cols, xseed=1)
+    for tokens in (1, 16, 64, 256, 1024):
+        x = xs[:tokens]
+        ref = oracle.bf16_to_f64(x) @ wt
+        for p in ((4, 3, 1, 2, 5) if tokens in (1, 256) else (4, 3)):
+            print(f"{rows}x{cols} tokens {tokens} pipeline {p} ({m.variant_in_use(tokens, p)[1]})", flush=True)
+            y = _run(env, m, x, p)
+            assert oracle.rel_err(y, ref) <= TOL, (tokens, p, oracle.rel_err(y, ref))
+
+
 @pytest.mark.parametrize("pipes", [(4, 4, 4), (3, 2, 1), (5, 5, 5)])
 def test_mlp_layer_8b_shapes(env, pipes):
     """The whole 8B-shaped SwiGLU layer through uw_mlp_forward (gate, up,
