@@ -96,11 +96,23 @@ __global__ __launch_bounds__(256) void palette_decode_kernel(const uint8_t* __re
     const u32x4 ev = *(const u32x4*)(side + ((size_t)m.y + rank) * 64 + q * 16);
     rebuild_exp(s, ev, p);
   }
-  const int kbn = cols >> 6;
-  const int64_t row = (b / kbn) * 16 + r;
-  uint16_t* o = out + row * cols + (b % kbn) * 64 + q * 16;
-  *(u32x4*)o = u32x4{p[0], p[1], p[2], p[3]};
-  *(u32x4*)(o + 8) = u32x4{p[4], p[5], p[6], p[7]};
+  // The brick's 16 rows x 128 bytes go through this wave's LDS (rows padded
+  // to 144 bytes) so that each store instruction writes 8 whole 128-byte row
+  // segments: lane l stores row 8 i + l / 8, bytes 16 (l % 8) .. + 15.
+  __shared__ __attribute__((aligned(16))) uint8_t tp[4][16 * 144];
+  uint8_t* t = tp[threadIdx.x >> 6];
+  *(u32x4*)(t + r * 144 + q * 32) = u32x4{p[0], p[1], p[2], p[3]};
+  *(u32x4*)(t + r * 144 + q * 32 + 16) = u32x4{p[4], p[5], p[6], p[7]};
+  __builtin_amdgcn_wave_barrier();
+  // (brick indices fit 32 bits: a matrix holds fewer than 2^31 weights)
+  const uint32_t kbn = (uint32_t)cols >> 6, bu = (uint32_t)b;
+  const uint32_t brow = bu / kbn, kb = bu - brow * kbn;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rr = 8 * i + (lane >> 3);
+    const u32x4 v = *(const u32x4*)(t + rr * 144 + (lane & 7) * 16);
+    *(u32x4*)(out + ((int64_t)brow * 16 + rr) * cols + kb * 64 + (lane & 7) * 8) = v;
+  }
 }
 
 }  // namespace
