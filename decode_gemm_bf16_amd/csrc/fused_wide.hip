@@ -340,20 +340,40 @@ __global__ __launch_bounds__(kThreads) void fused_wide_kernel(
   }
   wait_vm<0>();
 
+  // Epilogue through the wave's own (now idle) activation tile: a lane holds
+  // 4 consecutive rows of one token per accumulator group, so stored
+  // directly one instruction would write 32-byte pieces of 32 token rows.
+  // Per 32 tokens x 64 rows (8 KB) the wave writes its accumulators into
+  // LDS token-major (16-byte chunk c of token t at c ^ (t % 16)), then each
+  // store instruction writes 4 tokens' 256 contiguous bytes.
+  uint8_t* ep = xstage(0);
+  const int row0 = wbr0 * 16;
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int tb = 0; tb < kTBW; ++tb) {
 #pragma unroll
-    for (int tb = 0; tb < kTBW; ++tb) {
-      const int tok = tok0 + tb * 32 + (lane & 31);
-      if (tok >= tokens) continue;
+    for (int rh = 0; rh < 2; ++rh) {
+      const int t = lane & 31;
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int row = wbr0 * 16 + rb * 32 + 8 * v4 + 4 * (lane >> 5);
-        if (row >= rows) continue;
-        const f32x4 val = {acc[rb][tb][4 * v4 + 0], acc[rb][tb][4 * v4 + 1], acc[rb][tb][4 * v4 + 2],
-                           acc[rb][tb][4 * v4 + 3]};
-        *(f32x4*)(y + (size_t)tok * rows + row) = val;
+      for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int rb = 2 * rh + r2;
+          const int chunk = r2 * 8 + 2 * v4 + (lane >> 5);  // rows 4 chunk .. 4 chunk + 3 of the half
+          const f32x4 val = {acc[rb][tb][4 * v4 + 0], acc[rb][tb][4 * v4 + 1], acc[rb][tb][4 * v4 + 2],
+                             acc[rb][tb][4 * v4 + 3]};
+          *(f32x4*)(ep + t * 256 + ((chunk ^ (t & 15)) << 4)) = val;
+        }
+      __builtin_amdgcn_wave_barrier();
+      const int chunk = lane & 15;
+      const int row = row0 + rh * 64 + chunk * 4;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tt = 4 * j + (lane >> 4);
+        const f32x4 val = *(const f32x4*)(ep + tt * 256 + ((chunk ^ (tt & 15)) << 4));
+        const int tok = tok0 + tb * 32 + tt;
+        if (tok < tokens && row < rows) *(f32x4*)(y + (size_t)tok * rows + row) = val;
       }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
