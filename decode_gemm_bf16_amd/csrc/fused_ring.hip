@@ -288,20 +288,39 @@ __global__ __launch_bounds__(256) void fused_ring_kernel(
   for (int j = 0; j < D; ++j)
     if (kb + j < kbn) step(w[j], w[(j + 1) % D], a[j & 1], a[(j + 1) & 1], kb + j);
 
+  // Epilogue through LDS (the activation tiles, idle once every copy into
+  // them has landed and every wave has passed its last step): a lane holds 4
+  // consecutive rows of one token per accumulator group, so stored directly
+  // one instruction would write 16-byte pieces of 32 token rows.  Per 32
+  // rows x 32 tokens (4 KB of this wave's own LDS) the accumulators go in
+  // token-major (16-byte chunk c of token t at c ^ ((t / 2) % 8)), and each
+  // store instruction then writes 8 tokens' 128 contiguous bytes.
+  wait_vmcnt<0>();
+  __syncthreads();
+  uint8_t* ep = ring_lds + wave * 4096;
 #pragma unroll
   for (int i = 0; i < RB2; ++i) {
 #pragma unroll
     for (int t = 0; t < TB2; ++t) {
-      const int tok = tok0 + t * 32 + (lane & 31);
-      if (tok >= tokens) continue;
+      const int tw = lane & 31;
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const int row = (brow0 + 2 * i) * 16 + 8 * v4 + 4 * ks2;
-        if (row >= rows) continue;
+        const int chunk = 2 * v4 + ks2;  // rows 4 chunk .. 4 chunk + 3 of the block
         const f32x4 val = {acc[i][t][4 * v4 + 0], acc[i][t][4 * v4 + 1], acc[i][t][4 * v4 + 2],
                            acc[i][t][4 * v4 + 3]};
-        *(f32x4*)(y + (size_t)tok * rows + row) = val;
+        *(f32x4*)(ep + tw * 128 + ((chunk ^ ((tw >> 1) & 7)) << 4)) = val;
       }
+      __builtin_amdgcn_wave_barrier();
+      const int chunk = lane & 7;
+      const int row = (brow0 + 2 * i) * 16 + chunk * 4;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = 8 * j + (lane >> 3);
+        const f32x4 val = *(const f32x4*)(ep + tt * 128 + ((chunk ^ ((tt >> 1) & 7)) << 4));
+        const int tok = tok0 + t * 32 + tt;
+        if (tok < tokens && row < rows) *(f32x4*)(y + (size_t)tok * rows + row) = val;
+      }
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
