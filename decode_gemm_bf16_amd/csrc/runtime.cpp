@@ -146,6 +146,7 @@ uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, i
       if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
         const float alpha = 1.f, beta = 0.f;
         float best = 0.f;
+        bool have_best = false;  // a candidate ran and was timed (the first may fail to run)
         for (int i = 0; i < got; ++i) {
           // warm-up (and a check that the candidate runs)
           if (hipblasLtMatmul(g_blas, p.desc, &alpha, w, p.a, x, p.b, &beta, y, p.c, y, p.c, &res[i].algo,
@@ -165,8 +166,9 @@ uw_status gemm_bf16(const uint16_t* x, const uint16_t* w, float* y, int64_t m, i
             total += ms;
           }
           if (!ok) break;
-          if (i == 0 || total < best) {
+          if (!have_best || total < best) {
             best = total;
+            have_best = true;
             p.algo = res[i].algo;
           }
         }
