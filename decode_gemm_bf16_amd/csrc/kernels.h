@@ -108,8 +108,10 @@ struct HuffDev {
 };
 hipError_t launch_huff_decode(const HuffDev& h, DecodeEmit emit, void* out, hipStream_t s);
 
-// Palette form -> bf16 W row-major (decode without a Huffman stream).
-hipError_t launch_palette_decode(const FusedW& w, uint16_t* out, hipStream_t s);
+// Palette form -> bf16 W row-major (decode without a Huffman stream).  beside:
+// the decode runs on a side stream next to other kernels (a kernel that holds
+// no LDS, so that theirs find room).
+hipError_t launch_palette_decode(const FusedW& w, uint16_t* out, hipStream_t s, bool beside = false);
 
 hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, uint16_t* out, int64_t n, hipStream_t s);

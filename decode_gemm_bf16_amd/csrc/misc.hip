@@ -115,6 +115,39 @@ __global__ __launch_bounds__(256) void palette_decode_kernel(const uint8_t* __re
   }
 }
 
+// The same without LDS, each lane storing its own 32 bytes: for decodes on a
+// side stream beside the library GEMM, whose large tiles need a CU's LDS (a
+// decode workgroup holding 9 KB of LDS keeps a GEMM workgroup off its CU:
+// the 70B-shaped stack at 1024 tokens with the decodes overlapped ran 119.5
+// ms with the transposing kernel, 114.7 with this one).
+__global__ __launch_bounds__(256) void palette_decode_direct_kernel(
+    const uint8_t* __restrict__ sm, const uint8_t* __restrict__ nib, const uint2* __restrict__ meta,
+    const uint8_t* __restrict__ side, uint32_t lut0, uint32_t lut1, uint32_t lut2, uint32_t lut3,
+    uint16_t* __restrict__ out, int64_t bricks, int cols) {
+  const int64_t b = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  if (b >= bricks) return;
+  const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+  const uint32_t lut[4] = {lut0, lut1, lut2, lut3};
+  // the compressed streams are read once: non-temporal loads; the bf16 output
+  // is read next by the GEMM, so its stores keep the default policy
+  const uint64_t nw = (uint64_t)bricks * 1024;
+  const u32x4 s = ld16s(make_rsrc(sm, nw), lane * 16, (uint32_t)b * 1024);
+  const u32x2 n = ld8s(make_rsrc(nib, nw / 2), lane * 8, (uint32_t)b * 512);
+  const uint2 m = meta[b];
+  uint32_t p[8];
+  rebuild_palette(s, n, lut, p);
+  if ((m.x >> r) & 1u) {
+    const uint32_t rank = __builtin_popcount(m.x & ((1u << r) - 1u));
+    const u32x4 ev = *(const u32x4*)(side + ((size_t)m.y + rank) * 64 + q * 16);
+    rebuild_exp(s, ev, p);
+  }
+  const int kbn = cols >> 6;
+  const int64_t row = (b / kbn) * 16 + r;
+  uint16_t* o = out + row * cols + (b % kbn) * 64 + q * 16;
+  *(u32x4*)o = u32x4{p[0], p[1], p[2], p[3]};
+  *(u32x4*)(o + 8) = u32x4{p[4], p[5], p[6], p[7]};
+}
+
 }  // namespace
 
 hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t n, hipStream_t s) {
@@ -153,10 +186,15 @@ hipError_t launch_read(const void* src, void* sink, size_t bytes, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_palette_decode(const FusedW& w, uint16_t* out, hipStream_t s) {
+hipError_t launch_palette_decode(const FusedW& w, uint16_t* out, hipStream_t s, bool beside) {
   const int64_t bricks = w.rows * w.cols / 1024;
-  hipLaunchKernelGGL(palette_decode_kernel, dim3((unsigned)((bricks + 3) / 4)), dim3(256), 0, s, w.sm, w.codes,
-                     w.meta, w.side, w.lut[0], w.lut[1], w.lut[2], w.lut[3], out, bricks, (int)w.cols);
+  const dim3 grid((unsigned)((bricks + 3) / 4)), block(256);
+  if (beside)
+    hipLaunchKernelGGL(palette_decode_direct_kernel, grid, block, 0, s, w.sm, w.codes, w.meta, w.side, w.lut[0],
+                       w.lut[1], w.lut[2], w.lut[3], out, bricks, (int)w.cols);
+  else
+    hipLaunchKernelGGL(palette_decode_kernel, grid, block, 0, s, w.sm, w.codes, w.meta, w.side, w.lut[0], w.lut[1],
+                       w.lut[2], w.lut[3], out, bricks, (int)w.cols);
   return hipGetLastError();
 }
 

@@ -330,7 +330,7 @@ uw_status ensure_scratch(uw_matrix* h, int p) {
 
 uw_status launch_preprocess(uw_matrix* h, int p, hipStream_t s) {
   if (p == 5) {
-    UW_HIP(uw::launch_palette_decode(fused_view(h, false, h->d_nib), (uint16_t*)h->scratch, s));
+    UW_HIP(uw::launch_palette_decode(fused_view(h, false, h->d_nib), (uint16_t*)h->scratch, s, s != h->main));
     return UW_OK;
   }
   const uw::HuffDev d = huff_view(h);
