@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void palette_decode_kernel(const uint8_t* __re
 // side stream beside the library GEMM, whose large tiles need a CU's LDS (a
 // decode workgroup holding 9 KB of LDS keeps a GEMM workgroup off its CU:
 // the 70B-shaped stack at 1024 tokens with the decodes overlapped ran 119.5
-// ms with the transposing kernel, 114.7 with this one).
+// ms with the transposing kernel, 114.2 with this one).
 __global__ __launch_bounds__(256) void palette_decode_direct_kernel(
     const uint8_t* __restrict__ sm, const uint8_t* __restrict__ nib, const uint2* __restrict__ meta,
     const uint8_t* __restrict__ side, uint32_t lut0, uint32_t lut1, uint32_t lut2, uint32_t lut3,
